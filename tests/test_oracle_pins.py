@@ -1,0 +1,460 @@
+"""Pins of the fp64 oracle against things other than itself.
+
+Each check below fixes the oracle to a closed form, a 50-digit brute force of a
+different formula, a library routine (torch fp64 on the CPU), an invariant of
+the mathematics, or finite differences.  ``test_planted_mistakes`` plants
+plausible mistakes in the oracle (on the CPU) and checks that the core pins
+catch every one of them.
+
+Sources: "[RL] Avoid full-vocab gather for TP policy statistics" (torchtitan
+PR #4685), sections Summary, Why, and Correctness and compatibility; its review
+reply "Batch invariance under the patched logprob path" (Q1: plain
+cross-entropy and logsumexp + softmax on full logits; Q2: MAX combines exactly,
+SUM does not).
+"""
+import math
+
+import mpmath as mp
+import numpy as np
+import pytest
+
+import oracle.bi_oracle as orc
+from workloads import random_batch
+
+IGN = -100
+
+
+def fwd1(z, y):
+    lp, h, lse = orc.forward(np.asarray(z, dtype=np.float64)[None, :], np.array([y]))
+    return lp[0], h[0], lse[0]
+
+
+# ---------------------------------------------------------------- closed forms
+
+@pytest.mark.parametrize("V", [1, 2, 7, 1000, 151_936, 151_937])
+@pytest.mark.parametrize("c", [0.0, 3.5, -20.0, 250.0])
+def test_uniform_row(V, c):
+    z = np.full(V, c)
+    y = V // 3
+    lp, h, lse = fwd1(z, y)
+    assert lp == pytest.approx(-math.log(V), abs=1e-12)
+    assert h == pytest.approx(math.log(V), abs=1e-12)
+    assert lse == pytest.approx(c + math.log(V), rel=1e-15, abs=1e-12)
+    g = orc.backward(z[None, :], np.array([y]), np.array([lse]), np.array([0.75]))[0]
+    expect = np.full(V, 0.75 / V)
+    expect[y] = 0.75 * (1.0 / V - 1.0)
+    np.testing.assert_allclose(g, expect, rtol=1e-12, atol=1e-15)
+
+
+def test_qwen3_vocab_uniform_value():
+    # -ln 151936, the uniform-row logprob at the Qwen3 vocabulary size
+    lp, h, _ = fwd1(np.zeros(151_936), 5)
+    assert lp == pytest.approx(-11.931214658529285, abs=1e-12)
+    assert h == pytest.approx(11.931214658529285, abs=1e-12)
+
+
+@pytest.mark.parametrize("V,k,a,b", [(10, 3, 2.0, -1.0), (151_936, 17, 6.0, 0.5),
+                                     (5000, 4999, -3.0, 4.0)])
+def test_two_level_row(V, k, a, b):
+    z = np.full(V, b)
+    z[:k] = a
+    with mp.workdps(40):
+        Z = k * mp.e ** a + (V - k) * mp.e ** b
+        pa, pb = mp.e ** a / Z, mp.e ** b / Z
+        lse = mp.log(Z)
+        H = -(k * pa * mp.log(pa) + (V - k) * pb * mp.log(pb))
+    lp, h, l2 = fwd1(z, 0)
+    assert l2 == pytest.approx(float(lse), rel=1e-14)
+    assert lp == pytest.approx(float(a - lse), abs=1e-12)
+    assert h == pytest.approx(float(H), rel=1e-12)
+    lp_b, _, _ = fwd1(z, V - 1)
+    assert lp_b == pytest.approx(float(b - lse), abs=1e-12)
+
+
+@pytest.mark.parametrize("delta", [0.0, 1.0, 8.0, 30.0, 60.0])
+def test_dominant_logit(delta):
+    V, c, y = 151_936, -1.25, 4242
+    z = np.full(V, c)
+    z[y] = c + delta
+    lp, h, _ = fwd1(z, y)
+    with mp.workdps(50):
+        q = (V - 1) * mp.e ** (-delta)
+        exact_lp = -mp.log1p(q)
+        py = 1 / (1 + q)
+        po = mp.e ** (-delta) * py
+        exact_h = -(py * mp.log(py) + (V - 1) * po * mp.log(po))
+    assert lp == pytest.approx(float(exact_lp), abs=1e-12)
+    assert h == pytest.approx(float(exact_h), abs=1e-12, rel=1e-11)
+    if delta >= 60:
+        assert h < 1e-19   # entropy -> 0 for one dominant logit
+
+
+def test_v1_and_v2():
+    lp, h, lse = fwd1([3.0], 0)
+    assert (lp, h, lse) == (0.0, 0.0, 3.0)
+    g = orc.backward(np.array([[3.0]]), np.array([0]), np.array([lse]), np.array([2.0]))
+    assert g[0, 0] == 0.0
+    for zy, zo in [(0.3, -1.1), (-4.0, 7.5), (20.0, 20.0)]:
+        lp, h, _ = fwd1([zo, zy], 1)
+        x = zy - zo
+        assert lp == pytest.approx(-math.log1p(math.exp(-x)), abs=1e-14)
+        p = 1.0 / (1.0 + math.exp(-x))
+        hb = -(p * math.log(p) + (1 - p) * math.log(1 - p))
+        assert h == pytest.approx(hb, abs=1e-14)
+
+
+# ------------------------------------------------- brute force (mpmath, 50 digits)
+
+def _tiny_cases():
+    g = np.random.default_rng(7)
+    cases = []
+    for V in (1, 2, 3, 5, 8, 16):
+        for trial in range(4):
+            z = g.standard_normal(V) * 3.0
+            y = int(g.integers(0, V))
+            if V > 2 and trial == 1:
+                cols = [j for j in range(V) if j != y][: V // 3]
+                z[cols] = -np.inf
+            if trial == 2:
+                y = IGN
+            w = float(g.uniform(-1.0, 2.0))
+            cases.append((z, y, w))
+    return cases
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_brute_force(case):
+    z, y, w = _tiny_cases()[case]
+    blp, bh, blse, bg = orc.brute_force(z, y, w)
+    lp, h, lse = fwd1(z, y)
+    assert lse == pytest.approx(blse, rel=1e-14, abs=1e-14)
+    assert lp == pytest.approx(blp, abs=1e-13)
+    assert h == pytest.approx(bh, abs=1e-13)
+    g = orc.backward(z[None, :], np.array([y]), np.array([lse]), np.array([w]))[0]
+    np.testing.assert_allclose(g, bg, rtol=1e-12, atol=1e-14)
+
+
+# --------------------------------------------- library routine: torch fp64 (CPU)
+
+def test_torch_fp64_cross_entropy_entropy_and_grad():
+    torch = pytest.importorskip("torch")
+    F = torch.nn.functional
+    b = random_batch(48, 3001, "f32", seed=11, sigma=2.5, ignore_frac=0.1, mask_frac=0.1)
+    z = orc.decode(b.logits, "f32")
+    lp, h, lse = orc.forward(z, b.labels)
+    zt = torch.tensor(z, dtype=torch.float64, requires_grad=True)
+    yt = torch.tensor(b.labels)
+    ce = F.cross_entropy(zt, yt, reduction="none", ignore_index=IGN)
+    np.testing.assert_allclose(lp, -ce.detach().numpy(), rtol=0, atol=1e-12)
+    ent = torch.special.entr(torch.softmax(zt.detach(), dim=1)).sum(1).numpy()
+    np.testing.assert_allclose(h, ent, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lse, torch.logsumexp(zt.detach(), 1).numpy(), rtol=1e-14)
+    w = torch.tensor(b.weights, dtype=torch.float64)
+    (w * ce).sum().backward()
+    g = orc.backward(z, b.labels, lse, b.weights)
+    np.testing.assert_allclose(g, zt.grad.numpy(), rtol=1e-10, atol=1e-15)
+
+
+# ----------------------------------------------------------------- invariants
+
+def test_shift_invariance_and_bounds():
+    b = random_batch(16, 777, "f32", seed=3, sigma=4.0, mask_frac=0.2)
+    z = orc.decode(b.logits, "f32")
+    lp, h, lse = orc.forward(z, b.labels)
+    lp2, h2, lse2 = orc.forward(z + 123.5, b.labels)
+    np.testing.assert_allclose(lp2, lp, atol=1e-10)
+    np.testing.assert_allclose(h2, h, atol=1e-10)
+    np.testing.assert_allclose(lse2 - 123.5, lse, atol=1e-10)
+    nfin = np.isfinite(z).sum(1)
+    assert np.all(h >= -1e-15) and np.all(h <= np.log(nfin) + 1e-12)
+
+
+def test_gradient_invariants():
+    b = random_batch(32, 501, "f32", seed=5, ignore_frac=0.25, mask_frac=0.1)
+    z = orc.decode(b.logits, "f32")
+    lp, h, lse = orc.forward(z, b.labels)
+    g = orc.backward(z, b.labels, lse, b.weights)
+    for i, y in enumerate(b.labels):
+        if y == IGN:
+            assert np.all(g[i] == 0.0) and not np.any(np.signbit(g[i]))
+            continue
+        w = float(b.weights[i])
+        assert abs(g[i].sum()) < 1e-14 * max(1.0, w)
+        py = math.exp(lp[i])
+        assert g[i, y] == pytest.approx(w * (py - 1.0), rel=1e-12, abs=1e-16)
+        others = np.delete(g[i], y)
+        assert np.all(others >= 0.0)
+        assert np.all(g[i][np.isneginf(z[i])] == 0.0)
+
+
+def test_masked_row_equals_compacted_row():
+    b = random_batch(8, 400, "f32", seed=9, mask_frac=0.3, ignore_frac=0.0)
+    z = orc.decode(b.logits, "f32")
+    lp, h, lse = orc.forward(z, b.labels)
+    for i in range(8):
+        keep = np.isfinite(z[i])
+        zc = z[i][keep]
+        yc = int(np.count_nonzero(keep[: b.labels[i]]))
+        lpc, hc, lsec = fwd1(zc, yc)
+        assert lp[i] == pytest.approx(lpc, abs=1e-13)
+        assert h[i] == pytest.approx(hc, abs=1e-13)
+        assert lse[i] == pytest.approx(lsec, abs=1e-13)
+
+
+def test_ignored_rows_are_plus_zero_and_keep_entropy():
+    b = random_batch(6, 300, "f32", seed=1, ignore_frac=0.0)
+    z = orc.decode(b.logits, "f32")
+    ign = np.full(6, IGN)
+    lp, h, lse = orc.forward(z, ign)
+    lp_v, h_v, lse_v = orc.forward(z, b.labels)
+    assert np.all(lp == 0.0) and not np.any(np.signbit(lp))
+    np.testing.assert_array_equal(h, h_v)
+    np.testing.assert_array_equal(lse, lse_v)
+    g = orc.backward(z, ign, lse, b.weights)
+    assert np.all(g == 0.0) and not np.any(np.signbit(g))
+
+
+def test_bad_label_is_nan():
+    z = np.zeros((3, 10))
+    lp, h, lse = orc.forward(z, np.array([10, -1, 3]))
+    assert np.isnan(lp[0]) and np.isnan(lp[1]) and lp[2] == pytest.approx(-math.log(10))
+    assert np.isfinite(h).all()
+    g = orc.backward(z, np.array([10, -1, 3]), lse)
+    assert np.isnan(g[0]).all() and np.isnan(g[1]).all() and np.isfinite(g[2]).all()
+
+
+def test_fully_masked_row_natural_results():
+    lp, h, lse = fwd1([-np.inf] * 4, 1)
+    assert lse == -np.inf and np.isnan(lp) and np.isnan(h)
+
+
+# ------------------------------------------------- finite differences (V <= 16)
+
+@pytest.mark.parametrize("V", [2, 5, 16])
+def test_finite_differences(V):
+    g = np.random.default_rng(V)
+    z = g.standard_normal(V) * 2.0
+    y, w, hstep = int(g.integers(0, V)), 1.7, 1e-6
+    lp, _, lse = fwd1(z, y)
+    grad = orc.backward(z[None, :], np.array([y]), np.array([lse]), np.array([w]))[0]
+    for j in range(V):
+        zp, zm = z.copy(), z.copy()
+        zp[j] += hstep
+        zm[j] -= hstep
+        fd = (-w * fwd1(zp, y)[0] + w * fwd1(zm, y)[0]) / (2 * hstep)
+        assert grad[j] == pytest.approx(fd, abs=1e-8)
+
+
+# ------------------------------------------------------------ chunks + combine
+
+@pytest.mark.parametrize("bounds", [
+    [(0, 1000)],
+    [(0, 250), (250, 500), (500, 750), (750, 1000)],
+    [(0, 1), (1, 333), (333, 334), (334, 1000)],
+    [(j, j + 1) for j in range(1000)],
+])
+def test_chunk_combine_equals_full(bounds):
+    b = random_batch(12, 1000, "f32", seed=21, ignore_frac=0.2, mask_frac=0.05)
+    z = orc.decode(b.logits, "f32")
+    lp, h, lse = orc.forward(z, b.labels)
+    st = np.stack([orc.chunk_stats(z[:, a:e], b.labels, a, 1000) for a, e in bounds])
+    lp2, h2, lse2 = orc.combine(st, b.labels, 1000)
+    np.testing.assert_array_equal(st[:, :, 0].max(0), z.max(1))   # max is exact
+    np.testing.assert_allclose(lse2, lse, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lp2, lp, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(h2, h, rtol=0, atol=1e-12)
+    assert not np.any(np.signbit(lp2[b.labels == IGN]))
+
+
+def test_fully_masked_chunk_is_a_no_op():
+    b = random_batch(5, 600, "f32", seed=2, ignore_frac=0.0)
+    z = orc.decode(b.logits, "f32")
+    z[:, 200:400] = -np.inf
+    labels = np.where((b.labels >= 200) & (b.labels < 400), 0, b.labels)
+    lp, h, lse = orc.forward(z, labels)
+    bounds = [(0, 200), (200, 400), (400, 600)]
+    st = np.stack([orc.chunk_stats(z[:, a:e], labels, a, 600) for a, e in bounds])
+    assert np.all(st[1, :, 0] == -np.inf) and np.all(st[1, :, 1] == 0) and np.all(st[1, :, 3] == 0)
+    lp2, h2, lse2 = orc.combine(st, labels, 600)
+    np.testing.assert_allclose(np.stack([lp2, h2, lse2]), np.stack([lp, h, lse]), atol=1e-12)
+
+
+def test_chunk_uneven_qwen3_width():
+    # V = 151,937 split into 4 contiguous chunks (the last one ragged)
+    b = random_batch(3, 151_937, "f32", seed=4, mask_frac=0.1)
+    z = orc.decode(b.logits, "f32")
+    lp, h, lse = orc.forward(z, b.labels)
+    w = -(-151_937 // 4)
+    bounds = [(a, min(a + w, 151_937)) for a in range(0, 151_937, w)]
+    st = np.stack([orc.chunk_stats(z[:, a:e], b.labels, a, 151_937) for a, e in bounds])
+    lp2, h2, lse2 = orc.combine(st, b.labels, 151_937)
+    np.testing.assert_allclose(np.stack([lp2, h2, lse2]), np.stack([lp, h, lse]), atol=1e-12)
+
+
+def test_raw_weighted_sum_identity():
+    # sum exp(z - m) * z == U + m * S (the unshifted form of the 4th statistic)
+    b = random_batch(4, 257, "f32", seed=6)
+    z = orc.decode(b.logits, "f32")
+    m, S, U = orc.row_statistics(z)
+    raw = (np.exp(z - m[:, None]) * z).sum(1)
+    np.testing.assert_allclose(U + m * S, raw, rtol=1e-13, atol=1e-12)
+
+
+# ------------------------------------------------------------- input decoding
+
+def test_bf16_decode_known_patterns():
+    bits = np.array([0x3F80, 0xC000, 0xFF80, 0x7F80, 0x0001, 0x4049, 0x8000], dtype=np.uint16)
+    v = orc.decode(bits, "bf16")
+    assert v[0] == 1.0 and v[1] == -2.0 and v[2] == -np.inf and v[3] == np.inf
+    assert v[4] == 2.0 ** -133 and v[5] == 3.140625
+    assert v[6] == 0.0 and np.signbit(v[6])
+
+
+# ------------------------------------------------------------ planted mistakes
+
+def _pin_blocks():
+    """Compact versions of the pins, as (name, callable returning bool)."""
+
+    def uniform():
+        lp, h, lse = fwd1(np.full(1000, 2.0), 3)
+        return (abs(lp + math.log(1000)) < 1e-12 and abs(h - math.log(1000)) < 1e-12
+                and abs(lse - 2.0 - math.log(1000)) < 1e-12)
+
+    def dominant():
+        z = np.full(50, -1.0)
+        z[7] = 4.0
+        lp, _, _ = fwd1(z, 7)
+        return abs(lp + math.log1p(49 * math.exp(-5.0))) < 1e-12
+
+    def brute():
+        ok = True
+        for zz, y, w in _tiny_cases()[::3]:
+            blp, bh, blse, bg = orc.brute_force(zz, y, w)
+            lp, h, lse = fwd1(zz, y)
+            g = orc.backward(np.asarray(zz)[None, :], np.array([y]), np.array([lse]),
+                             np.array([w]))[0]
+            ok &= bool(abs(lp - blp) < 1e-12 and abs(h - bh) < 1e-12
+                       and abs(lse - blse) < 1e-12 and np.allclose(g, bg, atol=1e-12))
+        return ok
+
+    bb = random_batch(64, 64, "f32", seed=31, ignore_frac=0.1, mask_frac=0.1)
+
+    def square_batch():
+        # a square batch, so that a transposed operand shows
+        zb = orc.decode(bb.logits, "f32")
+        lp, h, lse = orc.forward(zb, bb.labels)
+        ok = True
+        for i in range(0, 64, 9):
+            blp, bh, _, _ = orc.brute_force(zb[i], int(bb.labels[i]), float(bb.weights[i]))
+            ok &= bool(abs(lp[i] - blp) < 1e-12 and abs(h[i] - bh) < 1e-12)
+        return ok
+
+    def combine():
+        zb = orc.decode(bb.logits, "f32")
+        lp, h, lse = orc.forward(zb, bb.labels)
+        st = np.stack([orc.chunk_stats(zb[:, a:e], bb.labels, a, 64)
+                       for a, e in [(0, 10), (10, 40), (40, 64)]])
+        lp2, h2, lse2 = orc.combine(st, bb.labels, 64)
+        return bool(np.allclose(lp2, lp, atol=1e-12) and np.allclose(h2, h, atol=1e-12)
+                    and np.allclose(lse2, lse, atol=1e-12))
+
+    def bf16():
+        return orc.decode(np.array([0x3F80, 0xC040], np.uint16), "bf16").tolist() == [1.0, -3.0]
+
+    return [("uniform", uniform), ("dominant", dominant), ("brute", brute),
+            ("square_batch", square_batch), ("combine", combine), ("bf16", bf16)]
+
+
+def _core_pin_failures():
+    """Run the compact pins; return the names of the failing ones."""
+    fails = []
+    for name, block in _pin_blocks():
+        try:
+            with np.errstate(all="ignore"):
+                ok = block()
+        except Exception:  # a crash is a failed pin too
+            ok = False
+        if not ok:
+            fails.append(name)
+    return fails
+
+
+def test_core_pins_pass_on_the_oracle():
+    assert _core_pin_failures() == []
+
+
+def _mutations():
+    o = orc
+    real = {n: getattr(o, n) for n in ("weighted_sum", "finalize", "denominator",
+                                       "target_logit", "backward", "combine", "decode",
+                                       "row_max", "softmax_from_lse")}
+
+    def drop_u(d, keep):
+        return np.zeros(d.shape[0])
+
+    def entropy_sign(m, S, U, t, kind):
+        lp, h, lse = real["finalize"](m, S, U, t, kind)
+        return lp, np.log(S) + U / S, lse
+
+    def no_shift(d, keep):
+        return np.where(keep, np.exp(np.where(keep, d + 1.0, 0.0)), 0.0).sum(axis=1)
+
+    def label_off_by_one(z, labels, ignore_index=IGN):
+        lab = np.where(labels == ignore_index, labels, (labels + 1) % z.shape[1])
+        return real["target_logit"](z, lab, ignore_index)
+
+    def grad_sign(z, labels, lse, weights=None, ignore_index=IGN):
+        return -real["backward"](z, labels, lse, weights, ignore_index)
+
+    def grad_no_weight(z, labels, lse, weights=None, ignore_index=IGN):
+        return real["backward"](z, labels, lse, None, ignore_index)
+
+    def combine_no_rescale(stats, labels, vocab, ignore_index=IGN):
+        st = np.array(stats, dtype=np.float64)
+        M = st[:, :, 0].max(0)
+        S = st[:, :, 1].sum(0)
+        U = st[:, :, 3].sum(0)
+        t = st[:, :, 2].sum(0)
+        return real["finalize"](M, S, U, t, o.label_kind(labels, vocab, ignore_index))
+
+    def combine_no_cross_term(stats, labels, vocab, ignore_index=IGN):
+        st = np.array(stats, dtype=np.float64)
+        M = st[:, :, 0].max(0)
+        a = np.exp(st[:, :, 0] - M)
+        S = (a * st[:, :, 1]).sum(0)
+        U = (a * st[:, :, 3]).sum(0)
+        t = st[:, :, 2].sum(0)
+        return real["finalize"](M, S, U, t, o.label_kind(labels, vocab, ignore_index))
+
+    def decode_shift15(logits, dtype):
+        if dtype == "bf16":
+            bits = np.asarray(logits, np.uint16).astype(np.uint32) << np.uint32(15)
+            return bits.view(np.float32).astype(np.float64)
+        return real["decode"](logits, dtype)
+
+    def transposed_max(z):
+        return z.max(axis=0)
+
+    def softmax_wrong_ref(z, lse):
+        return real["softmax_from_lse"](z, lse - 0.5)
+
+    return {
+        "drop_weighted_sum": ("weighted_sum", drop_u),
+        "entropy_sign": ("finalize", entropy_sign),
+        "denominator_shift": ("denominator", no_shift),
+        "label_off_by_one": ("target_logit", label_off_by_one),
+        "grad_sign": ("backward", grad_sign),
+        "grad_no_weight": ("backward", grad_no_weight),
+        "combine_no_rescale": ("combine", combine_no_rescale),
+        "combine_no_cross_term": ("combine", combine_no_cross_term),
+        "bf16_decode_shift": ("decode", decode_shift15),
+        "transposed_max": ("row_max", transposed_max),
+        "softmax_wrong_reference": ("softmax_from_lse", softmax_wrong_ref),
+    }
+
+
+@pytest.mark.parametrize("name", sorted(_mutations().keys()))
+def test_planted_mistakes(name, monkeypatch):
+    attr, fn = _mutations()[name]
+    monkeypatch.setattr(orc, attr, fn)
+    assert _core_pin_failures(), f"planted mistake {name!r} went unnoticed"
