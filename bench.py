@@ -1,0 +1,228 @@
+"""Benchmark: batch-invariant per-token logprob / entropy / gradient on one MI355X.
+
+One step is one pass of the hot path over a batch of 32,768 x 151,936 bf16
+logits (64 rollouts x 512 tokens, Qwen3 vocabulary): the full-row forward
+(logprob, entropy, lse) and the backward (bf16 grad = w * (softmax - onehot)).
+The vocabulary-chunked variant of the same step (4 x bi_vocab_chunk_stats of
+37,984 columns + bi_stats_combine, then the backward) is timed in the same run
+and reported under "chunked".  Inputs are seeded synthetic logits, resident in
+HBM before the timed region.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Prints one JSON line.  Kernel times come from HIP events recorded on the
+stream the kernels run on (torch's current stream).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "logits GB/s & rows/s fwd+bwd at 32768×151936 bf16; % of HBM peak"
+HBM_PEAK_GBPS = 8000.0     # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-rows", type=int, default=1024)
+    ap.add_argument("--profile-steps", type=int, default=None,
+                    help="run only this many steps (for profilers); still prints the line")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(vocab, e_in, e_grad, chunks):
+    """Bytes per row the method must move (read logits, labels; write outputs)."""
+    fwd = vocab * e_in + 8 + 12                # logits + label + (logprob, entropy, lse)
+    bwd = vocab * (e_in + e_grad) + 8 + 4 + 4  # logits + grad + label + lse + weight
+    chunk = vocab * e_in + chunks * (8 + 16)   # all chunks: logits + label + bi_stats each
+    combine = chunks * 16 + 8 + 12             # stats + label + outputs
+    return fwd, bwd, chunk, combine
+
+
+def cpu_baseline(rows_total, sample_rows, seed):
+    """The fp64 oracle (as it stands) on a bounded sample of the same workload."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+
+    import oracle.bi_oracle as orc
+    import workloads as wl
+
+    g = np.random.default_rng([seed, 77])
+    rows = np.sort(g.choice(rows_total, size=sample_rows, replace=False))
+    b = wl.draw(5, rows=rows, seed=seed)
+    threads = wl.default_threads()
+    block = 16
+
+    def run(a):
+        z = orc.decode(b.logits[a:a + block], "bf16")
+        lp, ent, lse = orc.forward(z, b.labels[a:a + block])
+        orc.backward(z, b.labels[a:a + block], lse, b.weights[a:a + block])
+
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(run, range(0, sample_rows, block)))
+    dt = time.perf_counter() - t0
+    return {"value": sample_rows / dt, "unit": "rows/s", "cores": threads, "kind": "oracle",
+            "sample": f"{sample_rows} seeded rows of the 32768x151936 bf16 workload, "
+                      f"fp64 numpy forward+backward, {threads} threads over 16-row blocks, "
+                      f"{dt:.2f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(rows shard across GPUs with no exchange, see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import entropy_bi_logprob_amd as bi
+    import workloads as wl
+
+    seed = wl.DEFAULT_SEED if args.seed is None else args.seed
+    w5 = wl.WORKLOADS[5]
+    N, V = w5.rows, w5.vocab
+
+    # inputs: drawn on the host (seeded, per row), then resident in HBM
+    t0 = time.perf_counter()
+    b = wl.draw(5, seed=seed)
+    gen_s = time.perf_counter() - t0
+    dev = torch.device("cuda:0")
+    logits = torch.from_numpy(b.logits.view(np.int16)).to(dev).view(torch.bfloat16)
+    labels = torch.from_numpy(b.labels).to(dev)
+    weights = torch.from_numpy(b.weights).to(dev)
+    del b
+    lp = torch.empty(N, dtype=torch.float32, device=dev)
+    ent = torch.empty_like(lp)
+    lse = torch.empty_like(lp)
+    grad = torch.empty((N, V), dtype=torch.bfloat16, device=dev)
+    bounds = wl.chunk_bounds(V, wl.LARGE_CHUNKS)
+    stats = torch.empty((len(bounds), N, 4), dtype=torch.float32, device=dev)
+    clp, cent, clse = torch.empty_like(lp), torch.empty_like(lp), torch.empty_like(lp)
+    flag = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    def step_full(ev=None):
+        if ev: ev[0].record(stream)
+        bi.fwd(logits, labels, out=(lp, ent, lse), status=flag, stream=stream)
+        if ev: ev[1].record(stream)
+        bi.bwd(logits, labels, lse, weights, out=grad, status=flag, stream=stream)
+        if ev: ev[2].record(stream)
+
+    def step_chunked(ev=None):
+        if ev: ev[0].record(stream)
+        for c, (a, e) in enumerate(bounds):
+            bi.vocab_chunk_stats(logits[:, a:e], labels, a, V, out=stats[c], status=flag,
+                                 stream=stream)
+        if ev: ev[1].record(stream)
+        bi.stats_combine(stats, labels, out=(clp, cent, clse), stream=stream)
+        if ev: ev[2].record(stream)
+        bi.bwd(logits, labels, clse, weights, out=grad, status=flag, stream=stream)
+        if ev: ev[3].record(stream)
+
+    steps = args.profile_steps or args.steps
+    warm = 0 if args.profile_steps else args.warmup
+    for _ in range(warm):
+        step_full()
+        step_chunked()
+    torch.cuda.synchronize()
+
+    # timed region: K full-row steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        step_full(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_fwd = [e[0].elapsed_time(e[1]) for e in evs]
+    t_bwd = [e[1].elapsed_time(e[2]) for e in evs]
+    ms_step = wall * 1e3 / steps
+
+    # the chunked variant of the step, same run
+    cevs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for k in range(steps):
+        step_chunked(cevs[k])
+    torch.cuda.synchronize()
+    cwall = time.perf_counter() - t1
+    t_chunk = [e[0].elapsed_time(e[1]) for e in cevs]
+    t_comb = [e[1].elapsed_time(e[2]) for e in cevs]
+    t_cbwd = [e[2].elapsed_time(e[3]) for e in cevs]
+    assert int(flag.item()) == 0
+
+    f_b, b_b, c_b, m_b = algorithmic_bytes(V, 2, 2, len(bounds))
+    med = lambda xs: float(np.median(xs))
+    mean = lambda xs: float(np.mean(xs))
+    fwd_ms, bwd_ms = mean(t_fwd), mean(t_bwd)
+    step_bytes = N * (f_b + b_b)
+    gbps = lambda nbytes, ms: nbytes / (ms * 1e-3) / 1e9
+    hbm = gbps(step_bytes, ms_step)
+    rows_s = N / (ms_step * 1e-3)
+    kernels = {
+        "fwd": {"ms": fwd_ms, "ms_median": med(t_fwd), "GBps": gbps(N * f_b, fwd_ms),
+                "bytes": N * f_b},
+        "bwd": {"ms": bwd_ms, "ms_median": med(t_bwd), "GBps": gbps(N * b_b, bwd_ms),
+                "bytes": N * b_b},
+    }
+    for k in kernels.values():
+        k["frac_of_peak"] = k["GBps"] / HBM_PEAK_GBPS
+    dom = max(kernels, key=lambda k: kernels[k]["ms"])
+    cms = cwall * 1e3 / steps
+    chunked = {
+        "ms_per_step": cms,
+        "rows_per_s": N / (cms * 1e-3),
+        "hbm_GBps": gbps(N * (c_b + m_b + b_b), cms),
+        "chunk_stats_ms_4x": mean(t_chunk), "combine_ms": mean(t_comb), "bwd_ms": mean(t_cbwd),
+        "chunk_stats_GBps": gbps(N * c_b, mean(t_chunk)),
+    }
+    line = {
+        "metric": METRIC,
+        "value": rows_s,
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warm,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "large_32768x151936_bf16", "rows": N, "vocab": V,
+                   "logits_dtype": "bf16", "grad_dtype": "bf16",
+                   "path": "full-row fwd + bwd", "seed": seed},
+        "logits_GBps": N * V * 2 / (ms_step * 1e-3) / 1e9,
+        "hbm_GBps": hbm,
+        "pct_hbm_peak": 100.0 * hbm / HBM_PEAK_GBPS,
+        "roofline": {"bound": "hbm", "achieved": kernels[dom]["GBps"], "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": kernels[dom]["GBps"] / HBM_PEAK_GBPS,
+                     "traffic": None, "kernel": f"{dom} (bf16 logits, bf16 grad)",
+                     "bytes_per_launch": kernels[dom]["bytes"]},
+        "kernels": kernels,
+        "chunked": chunked,
+        "input_gen_s": gen_s,
+    }
+    if not args.no_cpu_baseline and not args.profile_steps:
+        line["cpu_baseline"] = cpu_baseline(N, args.cpu_sample_rows, seed)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

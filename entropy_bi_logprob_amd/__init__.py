@@ -1,0 +1,263 @@
+"""Batch-invariant per-token logprob, entropy and gradient for MI355X (gfx950).
+
+A thin Python binding over the C ABI of ``libbi_logprob.so``
+(include/bi_logprob.h).  Every step of the computation runs in that library's
+HIP kernels; PyTorch only provides device memory and the current stream.  There
+is no fallback: if the library is missing, importing the binding's entry points
+raises.
+
+What is computed follows "[RL] Avoid full-vocab gather for TP policy
+statistics" (torchtitan PR #4685): per-token logprob (negated per-token
+cross-entropy) and exact entropy from full rows, the gradient
+``w * (softmax - onehot)``, and vocabulary-chunk statistics that combine
+exactly (sections Summary, Why, Correctness and compatibility).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch  # first: the library then binds to the HIP runtime torch has loaded
+
+__all__ = [
+    "IGNORE_INDEX", "BiError", "fwd", "bwd", "vocab_chunk_stats", "stats_combine",
+    "row_geometry", "LogprobEntropy", "logprob_entropy", "lib", "library_path",
+]
+
+IGNORE_INDEX = -100
+BI_F32, BI_BF16 = 0, 1
+BI_OK, BI_ERR_NULL, BI_ERR_SHAPE, BI_ERR_DTYPE, BI_ERR_ALIGN, BI_ERR_LAUNCH = range(6)
+BI_FLAG_BAD_LABEL = 1
+STATS_FIELDS = ("max", "sumexp", "target", "sumexp_logit")
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libbi_logprob.so"
+_lib = None
+
+
+class BiError(RuntimeError):
+    """A call into libbi_logprob failed."""
+
+    def __init__(self, fn: str, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{fn}: status {status} ({detail})")
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, _LIB_NAME)
+
+
+def _hip_runtimes_mapped():
+    paths = set()
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    paths.add(os.path.realpath(line.split()[-1]))
+    except OSError:  # pragma: no cover
+        pass
+    return paths
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library once (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is missing: build it with `python -m entropy_bi_logprob_amd.build` "
+            "(or __graft_entry__.build()); there is no fallback implementation")
+    L = ctypes.CDLL(path)
+    runtimes = _hip_runtimes_mapped()
+    if len(runtimes) > 1:
+        raise ImportError(f"two HIP runtimes are mapped into this process: {sorted(runtimes)}")
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.bi_logprob_fwd.argtypes = [vp, i32, i64, i64, i64, vp, i64, vp, vp, vp, vp, vp]
+    L.bi_logprob_bwd.argtypes = [vp, i32, i64, i64, i64, vp, i64, vp, vp, vp, i32, i64, vp, vp]
+    L.bi_vocab_chunk_stats.argtypes = [vp, i32, i64, i64, i64, i64, i64, vp, i64, vp, vp, vp]
+    L.bi_stats_combine.argtypes = [vp, i64, i64, vp, i64, vp, vp, vp, vp]
+    L.bi_row_geometry.argtypes = [i32, i64, ctypes.POINTER(i32), ctypes.POINTER(i32),
+                                  ctypes.POINTER(i32)]
+    for fn in ("bi_logprob_fwd", "bi_logprob_bwd", "bi_vocab_chunk_stats",
+               "bi_stats_combine", "bi_row_geometry"):
+        getattr(L, fn).restype = i32
+    L.bi_status_string.argtypes = [i32]
+    L.bi_status_string.restype = ctypes.c_char_p
+    L.bi_last_error.argtypes = []
+    L.bi_last_error.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(fn: str, status: int) -> None:
+    if status == BI_OK:
+        return
+    L = lib()
+    detail = (L.bi_last_error() or b"").decode() or L.bi_status_string(status).decode()
+    if status == BI_ERR_LAUNCH:
+        raise BiError(fn, status, detail)
+    raise ValueError(f"{fn}: {detail}")
+
+
+# ----------------------------------------------------------------- marshalling
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.float32:
+        return BI_F32
+    if dt == torch.bfloat16:
+        return BI_BF16
+    raise ValueError(f"logits must be float32 or bfloat16, got {dt}")
+
+
+def _rows(t: torch.Tensor, name: str) -> Tuple[int, int, int]:
+    """(n_rows, width, row_stride) of a 2-D device tensor with a contiguous last dim."""
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D [rows, width], got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    n, w = t.shape
+    if w > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have a contiguous last dimension")
+    return n, w, (t.stride(0) if n > 1 else w)
+
+
+def _vec(t: Optional[torch.Tensor], n: int, dtype: torch.dtype, name: str):
+    if t is None:
+        return None
+    if t.dtype != dtype or t.dim() != 1 or t.shape[0] != n or not t.is_cuda:
+        raise ValueError(f"{name} must be a device {dtype} vector of length {n}")
+    if n > 1 and t.stride(0) != 1:
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(int(getattr(stream, "cuda_stream", stream)))
+
+
+# ------------------------------------------------------------------ entry points
+
+def fwd(logits: torch.Tensor, labels: torch.Tensor, ignore_index: int = IGNORE_INDEX, *,
+        out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
+        status: Optional[torch.Tensor] = None, stream=None):
+    """(logprob, entropy, lse) fp32 [N] for full rows of ``logits`` [N, V]."""
+    n, v, rs = _rows(logits, "logits")
+    _vec(labels, n, torch.int64, "labels")
+    if out is None:
+        out = tuple(torch.empty(n, dtype=torch.float32, device=logits.device) for _ in range(3))
+    lp, ent, lse = (_vec(o, n, torch.float32, "out") for o in out)
+    _vec(status, 1, torch.int32, "status")
+    _check("bi_logprob_fwd", lib().bi_logprob_fwd(
+        _ptr(logits), _dtype_code(logits.dtype), n, v, rs, _ptr(labels), ignore_index,
+        _ptr(lp), _ptr(ent), _ptr(lse), _ptr(status), _stream(stream)))
+    return lp, ent, lse
+
+
+def bwd(logits: torch.Tensor, labels: torch.Tensor, lse: torch.Tensor,
+        weights: Optional[torch.Tensor] = None, grad_dtype: Optional[torch.dtype] = None,
+        ignore_index: int = IGNORE_INDEX, *, out: Optional[torch.Tensor] = None,
+        status: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """grad [N, V] = w * (softmax - onehot(label)) from the saved lse."""
+    n, v, rs = _rows(logits, "logits")
+    _vec(labels, n, torch.int64, "labels")
+    _vec(lse, n, torch.float32, "lse")
+    _vec(weights, n, torch.float32, "weights")
+    _vec(status, 1, torch.int32, "status")
+    if out is None:
+        out = torch.empty((n, v), dtype=grad_dtype or logits.dtype, device=logits.device)
+    gn, gv, grs = _rows(out, "grad")
+    if (gn, gv) != (n, v):
+        raise ValueError("grad must have the logits' shape")
+    _check("bi_logprob_bwd", lib().bi_logprob_bwd(
+        _ptr(logits), _dtype_code(logits.dtype), n, v, rs, _ptr(labels), ignore_index,
+        _ptr(lse), _ptr(weights), _ptr(out), _dtype_code(out.dtype), grs, _ptr(status),
+        _stream(stream)))
+    return out
+
+
+def vocab_chunk_stats(logits_chunk: torch.Tensor, labels: torch.Tensor, vocab_offset: int,
+                      vocab: Optional[int], ignore_index: int = IGNORE_INDEX, *,
+                      out: Optional[torch.Tensor] = None, status: Optional[torch.Tensor] = None,
+                      stream=None) -> torch.Tensor:
+    """[N, 4] fp32 statistics (max, sumexp, target, sumexp_logit) of one chunk.
+
+    ``logits_chunk`` is the [N, W] view of global columns
+    [vocab_offset, vocab_offset + W); ``vocab`` is the global vocabulary size
+    and is required.
+    """
+    if vocab is None:
+        raise ValueError("the global vocabulary size is required for vocabulary-chunk statistics")
+    n, w, rs = _rows(logits_chunk, "logits_chunk")
+    _vec(labels, n, torch.int64, "labels")
+    _vec(status, 1, torch.int32, "status")
+    if out is None:
+        out = torch.empty((n, 4), dtype=torch.float32, device=logits_chunk.device)
+    if out.shape != (n, 4) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 [N, 4] tensor")
+    _check("bi_vocab_chunk_stats", lib().bi_vocab_chunk_stats(
+        _ptr(logits_chunk), _dtype_code(logits_chunk.dtype), n, w, rs, vocab_offset, vocab,
+        _ptr(labels), ignore_index, _ptr(out), _ptr(status), _stream(stream)))
+    return out
+
+
+def stats_combine(stats: torch.Tensor, labels: torch.Tensor, ignore_index: int = IGNORE_INDEX, *,
+                  out=None, stream=None):
+    """Combine [C, N, 4] chunk statistics in chunk order -> (logprob, entropy, lse)."""
+    if stats.dim() != 3 or stats.shape[2] != 4 or stats.dtype != torch.float32 \
+            or not stats.is_contiguous() or not stats.is_cuda:
+        raise ValueError("stats must be a contiguous device float32 [C, N, 4] tensor")
+    c, n, _ = stats.shape
+    _vec(labels, n, torch.int64, "labels")
+    if out is None:
+        out = tuple(torch.empty(n, dtype=torch.float32, device=stats.device) for _ in range(3))
+    lp, ent, lse = (_vec(o, n, torch.float32, "out") for o in out)
+    _check("bi_stats_combine", lib().bi_stats_combine(
+        _ptr(stats), c, n, _ptr(labels), ignore_index, _ptr(lp), _ptr(ent), _ptr(lse),
+        _stream(stream)))
+    return lp, ent, lse
+
+
+def row_geometry(dtype: torch.dtype, width: int) -> Tuple[int, int, int]:
+    """(threads per workgroup, elements per 16-byte load, loads per rescale group)."""
+    a, b, c = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+    _check("bi_row_geometry", lib().bi_row_geometry(_dtype_code(dtype), width,
+                                                    ctypes.byref(a), ctypes.byref(b),
+                                                    ctypes.byref(c)))
+    return a.value, b.value, c.value
+
+
+# ----------------------------------------------------------------- autograd
+
+class LogprobEntropy(torch.autograd.Function):
+    """logprob (differentiable) and entropy (a metric, no gradient) of full rows."""
+
+    @staticmethod
+    def forward(ctx, logits, labels, ignore_index=IGNORE_INDEX, grad_dtype=None):
+        lp, ent, lse = fwd(logits, labels, ignore_index)
+        ctx.save_for_backward(logits, labels, lse)
+        ctx.ignore_index = ignore_index
+        ctx.grad_dtype = grad_dtype
+        ctx.mark_non_differentiable(ent)
+        return lp, ent
+
+    @staticmethod
+    def backward(ctx, grad_lp, grad_ent):
+        logits, labels, lse = ctx.saved_tensors
+        # d logprob / d z = onehot - softmax, so grad = (-g) * (softmax - onehot)
+        w = (-grad_lp).to(torch.float32).contiguous()
+        g = bwd(logits, labels, lse, w, ctx.grad_dtype or logits.dtype, ctx.ignore_index)
+        return g, None, None, None
+
+
+def logprob_entropy(logits, labels, ignore_index=IGNORE_INDEX, grad_dtype=None):
+    """Autograd-aware (logprob, entropy) of full rows."""
+    return LogprobEntropy.apply(logits, labels, ignore_index, grad_dtype)

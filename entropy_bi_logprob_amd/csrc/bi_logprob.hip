@@ -1,0 +1,913 @@
+// bi_logprob.hip - HIP kernels for gfx950 (CDNA4) and the C ABI declared in
+// include/bi_logprob.h: batch-invariant per-token logprob, entropy, gradient
+// and vocabulary-chunk statistics over large-vocabulary logits.
+//
+// What is computed comes from "[RL] Avoid full-vocab gather for TP policy
+// statistics" (torchtitan PR #4685): Summary and Why (logprob, exact entropy
+// from the global maximum, softmax denominator, target contribution and
+// entropy-weighted sum; gradient from the cross-entropy backward), Correctness
+// and compatibility (ignored labels, masked logits, weights, FP32/BF16, uneven
+// vocabulary), and the review reply "Batch invariance under the patched
+// logprob path" (bit equality needs a fixed summation grouping; max combines
+// exactly, sums do not).  How it is computed here is this file's own design.
+//
+// Design (all of it memory-bound; no matrix cores):
+//  * One workgroup reduces one row.  Its size T, the 16-byte vector width VEC
+//    and the rescale group are functions of (dtype, width) only.  Lane t owns
+//    the vectors v = k*T + t (k = 0, 1, ...) of the row, column v*VEC + s in
+//    slot s; vectors past the row's end are read as -inf, which adds exactly
+//    nothing.  The lane -> wave -> workgroup reduction tree is fixed.  Hence
+//    every row's bits are independent of the batch it sits in.
+//  * Each lane keeps (m, c, S, U) with a log2-domain reference c = -RN(m*log2e):
+//    S = sum 2^t, U = sum 2^t * t, t = fma(z, log2e, c).  One FMA and one
+//    v_exp_f32 per element; the reference is updated once per group of 16
+//    elements with an exact, always-executed rescale (a no-op when m is
+//    unchanged).  At the end lse = m + ln2*(log2 S - d) with the exact
+//    residual d = fma(m, log2e, c), and entropy = ln2*(log2 S - U/S).
+//  * -inf columns give 2^t = 0 and a clamped t (the 0 * -inf of the entropy
+//    term becomes 0); NaN logits still propagate through S.
+//  * The backward is elementwise from the saved lse: p = 2^((z - lse)*log2e),
+//    grad = w*p, and w*(p - 1) at the label column.
+//  * Loads and stores are 128-bit and non-temporal.  Rows need only be
+//    aligned to 4 bytes for vector access (gfx9 global loads accept
+//    dword-aligned dwordx4); bf16 rows on a 2-byte boundary take an element
+//    path with the same column map and arithmetic.
+
+#include <hip/hip_runtime.h>
+
+#include <float.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "bi_logprob.h"
+
+namespace {
+
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kLn2 = 0.693147180559945309417f;
+constexpr float kTFloor = -256.0f;   // 2^t == 0 in fp32 for every t below this
+constexpr int kMaxThreads = 1024;
+constexpr int kMaxWaves = kMaxThreads / 64;
+constexpr int64_t kMaxWidth = int64_t(1) << 29;
+
+#ifndef BI_GROUP_ELEMS
+#define BI_GROUP_ELEMS 16
+#endif
+#ifndef BI_MIN_VECS_PER_LANE
+#define BI_MIN_VECS_PER_LANE 8
+#endif
+constexpr int kGroupElems = BI_GROUP_ELEMS;   // elements per lane per rescale
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+struct Geometry {
+  int threads;  // workgroup size
+  int vec;      // elements per 16-byte vector
+  int group;    // vectors per rescale group
+};
+
+// The batch-invariance contract: a function of (dtype, width) only.
+__host__ __device__ inline Geometry row_geometry(int dtype, int64_t width) {
+  Geometry g;
+  g.vec = dtype == BI_BF16 ? 8 : 4;
+  g.group = kGroupElems / g.vec;
+  const int64_t nvec = (width + g.vec - 1) / g.vec;
+  int t = 64;
+  while (t < kMaxThreads && int64_t(t) * BI_MIN_VECS_PER_LANE < nvec) t *= 2;
+  g.threads = t;
+  return g;
+}
+
+// ------------------------------------------------------------------ elements
+
+template <int DT>
+struct Elt;
+
+template <>
+struct Elt<BI_F32> {
+  static constexpr int VEC = 4;
+  __device__ static inline void decode(const u32x4& r, float* z) {
+    z[0] = __uint_as_float(r.x);
+    z[1] = __uint_as_float(r.y);
+    z[2] = __uint_as_float(r.z);
+    z[3] = __uint_as_float(r.w);
+  }
+  __device__ static inline float load1(const char* row, int64_t j) {
+    return reinterpret_cast<const float*>(row)[j];
+  }
+};
+
+template <>
+struct Elt<BI_BF16> {
+  static constexpr int VEC = 8;
+  // element 2k is the low half of dword k (little endian)
+  __device__ static inline void decode(const u32x4& r, float* z) {
+    z[0] = __uint_as_float(r.x << 16);
+    z[1] = __uint_as_float(r.x & 0xffff0000u);
+    z[2] = __uint_as_float(r.y << 16);
+    z[3] = __uint_as_float(r.y & 0xffff0000u);
+    z[4] = __uint_as_float(r.z << 16);
+    z[5] = __uint_as_float(r.z & 0xffff0000u);
+    z[6] = __uint_as_float(r.w << 16);
+    z[7] = __uint_as_float(r.w & 0xffff0000u);
+  }
+  __device__ static inline float load1(const char* row, int64_t j) {
+    return __uint_as_float(uint32_t(reinterpret_cast<const uint16_t*>(row)[j]) << 16);
+  }
+};
+
+// Where one lane reads its vectors of a row.  Vector k*T + tid of the row
+// (step k) sits at byte k*T*16 + tid*16.  The 4-byte-aligned path reads it
+// with one non-temporal buffer_load_dwordx4: the lane's offset is a constant
+// VGPR and the step offset an SGPR, so addressing costs no vector ALU.  A bf16
+// row on a 2-byte boundary is read with element loads into the same bits.
+struct RowSrc {
+  __amdgpu_buffer_rsrc_t rs;
+  const char* row;
+  uint32_t lane_off;    // tid * 16
+  uint32_t step_bytes;  // T * 16
+};
+
+constexpr int kNonTemporal = 2;          // cache policy bits: nt
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format
+
+__device__ inline RowSrc row_src(const char* row, int64_t row_bytes, int T, int tid) {
+  RowSrc s;
+  s.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(row), (short)0,
+                                           int(row_bytes), kRsrcWord3);
+  s.row = row;
+  s.lane_off = uint32_t(tid) * 16u;
+  s.step_bytes = uint32_t(T) * 16u;
+  return s;
+}
+
+template <bool VLOAD>
+__device__ inline u32x4 fetch(const RowSrc& s, uint32_t k) {
+  if constexpr (VLOAD) {
+    return __builtin_amdgcn_raw_buffer_load_b128(s.rs, s.lane_off, k * s.step_bytes, kNonTemporal);
+  } else {
+    const uint16_t* p = reinterpret_cast<const uint16_t*>(s.row + k * s.step_bytes + s.lane_off);
+    u32x4 r;
+    r.x = uint32_t(p[0]) | (uint32_t(p[1]) << 16);
+    r.y = uint32_t(p[2]) | (uint32_t(p[3]) << 16);
+    r.z = uint32_t(p[4]) | (uint32_t(p[5]) << 16);
+    r.w = uint32_t(p[6]) | (uint32_t(p[7]) << 16);
+    return r;
+  }
+}
+
+// v_max3_f32 without the canonicalizing moves fmaxf would add around
+// non-arithmetic inputs (decoded bits).  NaN inputs still reach the sums.
+__device__ inline float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+__device__ inline float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ inline float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
+
+// log2-domain reference of a running max: c = -RN(m*log2e), kept finite for
+// m = -inf (an empty lane) so that no inf - inf arises.
+__device__ inline float ref_of(float m) { return fminf(-(m * kLog2e), FLT_MAX); }
+
+// --------------------------------------------------------- lane accumulator
+
+struct Acc {
+  float m;  // running max of the logits seen
+  float c;  // ref_of(m)
+  float S;  // sum of 2^t
+  float U;  // sum of 2^t * t   (log2 units, about c)
+};
+
+__device__ inline Acc acc_empty() { return Acc{-INFINITY, FLT_MAX, 0.0f, 0.0f}; }
+
+// Move an accumulator to the reference C (C <= a.c).  Exact no-op for C == a.c.
+__device__ inline void rebase(Acc& a, float C) {
+  const float d = fmaxf(C - a.c, kTFloor);
+  const float f = exp2_hw(d);
+  a.U = f * fmaf(d, a.S, a.U);
+  a.S = f * a.S;
+  a.c = C;
+}
+
+// max of K values through a fixed tree of v_max3 (K - 1 values removed per
+// two-operand step, so ceil((K - 1) / 2) instructions)
+template <int K>
+__device__ inline float max_reduce(const float* v) {
+  if constexpr (K == 1) {
+    return v[0];
+  } else if constexpr (K == 2) {
+    return max3(v[0], v[1], v[1]);
+  } else {
+    constexpr int Q = K / 3, R = K % 3;
+    float w[Q + R];
+#pragma unroll
+    for (int j = 0; j < Q; ++j) w[j] = max3(v[3 * j], v[3 * j + 1], v[3 * j + 2]);
+#pragma unroll
+    for (int r = 0; r < R; ++r) w[Q + r] = v[3 * Q + r];
+    return max_reduce<Q + R>(w);
+  }
+}
+
+template <int N>
+__device__ inline float tree_max(const float* z, float m) {
+  float v[N + 1];
+  v[0] = m;
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i + 1] = z[i];
+  return max_reduce<N + 1>(v);
+}
+
+template <int VEC>
+__device__ inline float tree_sum(const float* e) {
+  if constexpr (VEC == 8) {
+    return ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+  } else {
+    return (e[0] + e[1]) + (e[2] + e[3]);
+  }
+}
+
+// Accumulate NV vectors (NV*VEC decoded values, in lane order) into `a`.
+template <int VEC, int NV>
+__device__ inline void accumulate(Acc& a, const float* z) {
+  const float mx = tree_max<NV * VEC>(z, a.m);
+  const float c = ref_of(mx);
+  rebase(a, c);
+  a.m = mx;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    float e[VEC], tc[VEC];
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) {
+      const float t = fmaf(z[j * VEC + k], kLog2e, c);
+      e[k] = exp2_hw(t);              // 0 for z = -inf; NaN for NaN z
+      tc[k] = fmaxf(t, kTFloor);      // finite, so 0 * tc == 0 for masked columns
+    }
+    float u = e[0] * tc[0];
+#pragma unroll
+    for (int k = 1; k < VEC; ++k) u = fmaf(e[k], tc[k], u);
+    a.S += tree_sum<VEC>(e);
+    a.U += u;
+  }
+}
+
+template <int DT, int G, bool VLOAD>
+__device__ inline void load_group(u32x4* buf, const RowSrc& src, uint32_t g) {
+#pragma unroll
+  for (int i = 0; i < G; ++i) buf[i] = fetch<VLOAD>(src, g * G + i);
+}
+
+// Run body(buffer, g) over groups g = 0 .. n-1 of G steps each, with group
+// g+1's loads issued before group g is processed.  Two register buffers are
+// used in turn and the last group is peeled, so that every processing site
+// sees the same unconditional loads ahead of it and waits only for its own.
+template <int DT, int G, bool VLOAD, typename Body>
+__device__ inline void pipelined_groups(const RowSrc& src, uint32_t n, Body&& body) {
+  if (n == 0) return;
+  u32x4 A[G], B[G];
+  load_group<DT, G, VLOAD>(A, src, 0);
+  for (uint32_t g = 0;;) {
+    if (g + 1 == n) {
+      body(A, g);
+      return;
+    }
+    load_group<DT, G, VLOAD>(B, src, g + 1);
+    body(A, g);
+    ++g;
+    if (g + 1 == n) {
+      body(B, g);
+      return;
+    }
+    load_group<DT, G, VLOAD>(A, src, g + 1);
+    body(B, g);
+    ++g;
+  }
+}
+
+template <int DT, int G>
+__device__ inline void accumulate_group(Acc& a, const u32x4* buf) {
+  constexpr int VEC = Elt<DT>::VEC;
+  float z[G * VEC];
+#pragma unroll
+  for (int i = 0; i < G; ++i) Elt<DT>::decode(buf[i], z + i * VEC);
+  accumulate<VEC, G>(a, z);
+}
+
+// Scan one row segment of `width` columns: every lane accumulates its vectors.
+// Full groups run with the next group's loads in flight (two register
+// buffers used in turn), then single full steps, then the one ragged step.
+template <int DT, bool VLOAD>
+__device__ inline void row_scan(Acc& a, const RowSrc& src, int64_t width, int T, int tid) {
+  constexpr int VEC = Elt<DT>::VEC;
+  constexpr int G = kGroupElems / VEC;
+  const uint32_t nfull = uint32_t(width / VEC);
+  const uint32_t nvec = uint32_t((width + VEC - 1) / VEC);
+  const uint32_t full_steps = nfull / uint32_t(T);
+  const uint32_t ngroups = full_steps / G;
+
+  pipelined_groups<DT, G, VLOAD>(src, ngroups, [&](const u32x4* buf, uint32_t) {
+    accumulate_group<DT, G>(a, buf);
+  });
+  for (uint32_t k = ngroups * G; k < full_steps; ++k) {
+    float z[VEC];
+    Elt<DT>::decode(fetch<VLOAD>(src, k), z);
+    accumulate<VEC, 1>(a, z);
+  }
+  if (full_steps * uint32_t(T) < nvec) {
+    const uint32_t v = full_steps * uint32_t(T) + tid;
+    float z[VEC];
+    if (v < nfull) {
+      Elt<DT>::decode(fetch<VLOAD>(src, full_steps), z);
+    } else {
+#pragma unroll
+      for (int k = 0; k < VEC; ++k) {
+        const int64_t j = int64_t(v) * VEC + k;
+        z[k] = j < width ? Elt<DT>::load1(src.row, j) : -INFINITY;
+      }
+    }
+    accumulate<VEC, 1>(a, z);
+  }
+}
+
+// ------------------------------------------------- fixed reduction tree
+
+template <int CTRL>
+__device__ inline float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+constexpr int kQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+
+__device__ inline float swizzle_xor16(float x) {
+  // ds_swizzle bit mode: and_mask 0x1f, or_mask 0, xor_mask 0x10
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
+}
+__device__ inline float lane_value(float x, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+
+// max / sum over each 16-lane row (result in every lane of the row)
+__device__ inline float row16_max(float m) {
+  m = fmaxf(m, dpp<kQuadXor1>(m));
+  m = fmaxf(m, dpp<kQuadXor2>(m));
+  m = fmaxf(m, dpp<kRowHalfMirror>(m));
+  return fmaxf(m, dpp<kRowMirror>(m));
+}
+__device__ inline float row16_sum(float s) {
+  s = s + dpp<kQuadXor1>(s);
+  s = s + dpp<kQuadXor2>(s);
+  s = s + dpp<kRowHalfMirror>(s);
+  return s + dpp<kRowMirror>(s);
+}
+// whole wave: rows -> halves (swizzle) -> lanes 0 and 32 (uniform result)
+__device__ inline float wave_max(float m) {
+  m = row16_max(m);
+  m = fmaxf(m, swizzle_xor16(m));
+  return fmaxf(lane_value(m, 0), lane_value(m, 32));
+}
+__device__ inline float wave_sum(float s) {
+  s = row16_sum(s);
+  s = s + swizzle_xor16(s);
+  return lane_value(s, 0) + lane_value(s, 32);
+}
+
+// Reduce the lanes' accumulators of one workgroup; the result is returned
+// (uniformly) in wave 0.  Lanes: max, rebase to the common reference, sums.
+// Waves: the same over the per-wave results, read from LDS by wave 0.
+__device__ inline Acc block_reduce(Acc a, float* lds, int T, int tid) {
+  const float wm = wave_max(a.m);
+  rebase(a, ref_of(wm));
+  Acc w;
+  w.m = wm;
+  w.c = a.c;
+  w.S = wave_sum(a.S);
+  w.U = wave_sum(a.U);
+  const int wave = tid >> 6, nw = T >> 6;
+  if (nw == 1) return w;
+  if ((tid & 63) == 0) {
+    lds[wave] = w.m;
+    lds[kMaxWaves + wave] = w.S;
+    lds[2 * kMaxWaves + wave] = w.U;
+  }
+  __syncthreads();
+  Acc r = acc_empty();
+  if (wave == 0) {
+    const int l = tid;
+    Acc b = acc_empty();
+    if (l < nw) {
+      b.m = lds[l];
+      b.c = ref_of(b.m);
+      b.S = lds[kMaxWaves + l];
+      b.U = lds[2 * kMaxWaves + l];
+    }
+    const float bm = lane_value(row16_max(b.m), 0);
+    rebase(b, ref_of(bm));
+    r.m = bm;
+    r.c = b.c;
+    r.S = lane_value(row16_sum(b.S), 0);
+    r.U = lane_value(row16_sum(b.U), 0);
+  }
+  return r;
+}
+
+// lse about the exact max: m + ln2*(log2 S - d), d = m*log2e + c exactly.
+__device__ inline float lse_of(const Acc& r) {
+  const float d = fmaf(r.m, kLog2e, r.c);
+  return r.S == 0.0f ? -INFINITY : r.m + kLn2 * (log2_hw(r.S) - d);
+}
+__device__ inline float entropy_of(const Acc& r) {
+  return kLn2 * (log2_hw(r.S) - r.U / r.S);
+}
+
+// ---------------------------------------------------------------- kernels
+
+struct FwdArgs {
+  const char* logits;
+  int64_t n_rows, width, row_bytes;   // width = vocab or chunk width
+  int64_t vocab, vocab_offset;        // label range [0, vocab); chunk start
+  const int64_t* labels;
+  int64_t ignore_index;
+  float* logprob;
+  float* entropy;
+  float* lse;
+  bi_stats* stats;                    // chunk mode output
+  int32_t* status_flag;
+};
+
+enum { kFull = 0, kChunk = 1 };
+
+// ALIGNED: every row starts on a 4-byte boundary (checked on the host), so
+// only the vector path is compiled in; otherwise each row picks its path.
+template <int DT, int MODE, bool ALIGNED>
+__global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(8)))
+void fwd_kernel(FwdArgs p) {
+  __shared__ float lds[3 * kMaxWaves];
+  const int T = blockDim.x, tid = threadIdx.x;
+  for (int64_t row = blockIdx.x; row < p.n_rows; row += gridDim.x) {
+    const char* rp = p.logits + row * p.row_bytes;
+    // the label's logit, loaded by thread 0 before the scan
+    const int64_t y = p.labels[row];
+    const bool ignored = y == p.ignore_index;
+    const bool bad = !ignored && (y < 0 || y >= p.vocab);
+    const int64_t local = y - p.vocab_offset;
+    const bool inside = !ignored && !bad && local >= 0 && local < p.width;
+    float zy = 0.0f;
+    if (tid == 0 && inside) zy = Elt<DT>::load1(rp, local);
+
+    Acc a = acc_empty();
+    const RowSrc src = row_src(rp, p.width * (DT == BI_BF16 ? 2 : 4), T, tid);
+    if (ALIGNED || (reinterpret_cast<uintptr_t>(rp) & 3u) == 0) {
+      row_scan<DT, true>(a, src, p.width, T, tid);
+    } else {
+      row_scan<DT, false>(a, src, p.width, T, tid);
+    }
+    const Acc r = block_reduce(a, lds, T, tid);
+    if (tid == 0) {
+      if (bad && p.status_flag) atomicOr(p.status_flag, BI_FLAG_BAD_LABEL);
+      if constexpr (MODE == kFull) {
+        const float lse = lse_of(r);
+        if (p.lse) p.lse[row] = lse;
+        if (p.entropy) p.entropy[row] = entropy_of(r);
+        if (p.logprob) p.logprob[row] = bad ? NAN : (ignored ? 0.0f : zy - lse);
+      } else {
+        // natural-units statistics about the exact max m
+        const float d = fmaf(r.m, kLog2e, r.c);
+        const float f = exp2_hw(-d);
+        bi_stats s;
+        s.max = r.m;
+        s.sumexp = r.S == 0.0f ? 0.0f : r.S * f;
+        s.sumexp_logit = r.S == 0.0f ? 0.0f : kLn2 * (fmaf(-d, r.S, r.U) * f);
+        s.target = bad ? NAN : (inside ? zy : 0.0f);
+        p.stats[row] = s;
+      }
+    }
+    if (row + gridDim.x < p.n_rows) __syncthreads();   // lds reused by the next row
+  }
+}
+
+__device__ inline uint32_t pack_bf16x2(float lo, float hi) {
+  // round to nearest even (v_cvt_pk_bf16_f32)
+  const __bf16 a = __bf16(lo), b = __bf16(hi);
+  return uint32_t(__builtin_bit_cast(uint16_t, a)) | (uint32_t(__builtin_bit_cast(uint16_t, b)) << 16);
+}
+
+// Where one lane writes the gradients of its vectors: vector k*T + tid holds
+// VEC values of GSIZE bytes each.  The 4-byte-aligned path uses non-temporal
+// buffer_store_dwordx4 (lane offset in a VGPR, step offset in an SGPR).
+template <int GT, int VEC>
+struct RowDst {
+  static constexpr int kBytes = VEC * (GT == BI_BF16 ? 2 : 4);   // per vector
+  __amdgpu_buffer_rsrc_t rs;
+  char* row;
+  uint32_t lane_off, step_bytes;
+
+  __device__ RowDst(char* r, int64_t row_bytes, int T, int tid) {
+    rs = __builtin_amdgcn_make_buffer_rsrc(r, (short)0, int(row_bytes), kRsrcWord3);
+    row = r;
+    lane_off = uint32_t(tid) * kBytes;
+    step_bytes = uint32_t(T) * kBytes;
+  }
+
+  template <bool VSTORE>
+  __device__ inline void store(uint32_t k, const float* g) const {
+    u32x4 w[kBytes / 16];
+    if constexpr (GT == BI_BF16) {
+      static_assert(VEC == 8, "bf16 gradients come from bf16 logits");
+      w[0].x = pack_bf16x2(g[0], g[1]);
+      w[0].y = pack_bf16x2(g[2], g[3]);
+      w[0].z = pack_bf16x2(g[4], g[5]);
+      w[0].w = pack_bf16x2(g[6], g[7]);
+    } else {
+#pragma unroll
+      for (int h = 0; h < VEC / 4; ++h) {
+        w[h].x = __float_as_uint(g[4 * h + 0]);
+        w[h].y = __float_as_uint(g[4 * h + 1]);
+        w[h].z = __float_as_uint(g[4 * h + 2]);
+        w[h].w = __float_as_uint(g[4 * h + 3]);
+      }
+    }
+    if constexpr (VSTORE) {
+#pragma unroll
+      for (int h = 0; h < kBytes / 16; ++h)
+        __builtin_amdgcn_raw_buffer_store_b128(w[h], rs, lane_off + 16u * h, k * step_bytes,
+                                               kNonTemporal);
+    } else {
+      uint16_t* q = reinterpret_cast<uint16_t*>(row + k * step_bytes + lane_off);
+#pragma unroll
+      for (int h = 0; h < kBytes / 16; ++h) {
+        q[8 * h + 0] = uint16_t(w[h].x); q[8 * h + 1] = uint16_t(w[h].x >> 16);
+        q[8 * h + 2] = uint16_t(w[h].y); q[8 * h + 3] = uint16_t(w[h].y >> 16);
+        q[8 * h + 4] = uint16_t(w[h].z); q[8 * h + 5] = uint16_t(w[h].z >> 16);
+        q[8 * h + 6] = uint16_t(w[h].w); q[8 * h + 7] = uint16_t(w[h].w >> 16);
+      }
+    }
+  }
+
+  __device__ inline void store1(int64_t j, float g) const {
+    if constexpr (GT == BI_BF16) {
+      const __bf16 b = __bf16(g);
+      reinterpret_cast<uint16_t*>(row)[j] = __builtin_bit_cast(uint16_t, b);
+    } else {
+      reinterpret_cast<float*>(row)[j] = g;
+    }
+  }
+};
+
+// p = 2^((z - lse) * log2e): the subtraction first keeps the relative error
+// of p small even for logits far from zero.
+__device__ inline float prob(float z, float lse) { return exp2_hw((z - lse) * kLog2e); }
+
+template <int VEC>
+__device__ inline void grad_vec(const float* z, float lse, float w, float* g) {
+#pragma unroll
+  for (int k = 0; k < VEC; ++k) g[k] = w * prob(z[k], lse);
+}
+
+// the label column gets w * (p - 1)
+template <int VEC>
+__device__ inline void grad_label(const float* z, float lse, float w, int slot, float* g) {
+#pragma unroll
+  for (int k = 0; k < VEC; ++k)
+    if (k == slot) g[k] = w * (prob(z[k], lse) - 1.0f);
+}
+
+struct BwdArgs {
+  const char* logits;
+  char* grad;
+  int64_t n_rows, vocab, row_bytes, grad_row_bytes;
+  const int64_t* labels;
+  int64_t ignore_index;
+  const float* lse;
+  const float* weights;
+  int32_t* status_flag;
+};
+
+template <int DT, int GT, bool VLOAD, bool VSTORE>
+__device__ inline void bwd_vec(const RowDst<GT, Elt<DT>::VEC>& dst, uint32_t k, const u32x4& raw,
+                               float lse, float w, uint32_t label_lane, int slot, int tid) {
+  constexpr int VEC = Elt<DT>::VEC;
+  float z[VEC], g[VEC];
+  Elt<DT>::decode(raw, z);
+  grad_vec<VEC>(z, lse, w, g);
+  if (uint32_t(tid) == label_lane) grad_label<VEC>(z, lse, w, slot, g);
+  dst.template store<VSTORE>(k, g);
+}
+
+template <int DT, int GT, bool VLOAD, bool VSTORE>
+__device__ inline void bwd_row(const BwdArgs& p, const RowSrc& src,
+                               const RowDst<GT, Elt<DT>::VEC>& dst, int64_t y, int kind,
+                               float lse, float w, int T, int tid) {
+  constexpr int VEC = Elt<DT>::VEC;
+  constexpr int G = kGroupElems / VEC;
+  const int64_t width = p.vocab;
+  const uint32_t nfull = uint32_t(width / VEC);
+  const uint32_t nvec = uint32_t((width + VEC - 1) / VEC);
+  const uint32_t full_steps = nfull / uint32_t(T);
+  // the label's vector is yv = k*T + lane: lane = yv - k*T in step k
+  const uint32_t yv = kind == 0 ? uint32_t(y / VEC) : 0xffffffffu;
+  const int slot = int(y % VEC);
+
+  if (kind != 0) {   // ignored rows: +0.0; bad labels: NaN; logits not read
+    float g[VEC];
+    const float fill = kind == 1 ? 0.0f : NAN;
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) g[k] = fill;
+    for (uint32_t k = 0; k < full_steps; ++k) dst.template store<VSTORE>(k, g);
+    const uint32_t v = full_steps * uint32_t(T) + tid;
+    if (v < nfull) dst.template store<VSTORE>(full_steps, g);
+    else if (v == nfull)
+      for (int64_t j = int64_t(v) * VEC; j < width; ++j) dst.store1(j, fill);
+    return;
+  }
+  const uint32_t ngroups = full_steps / G;
+  pipelined_groups<DT, G, VLOAD>(src, ngroups, [&](const u32x4* buf, uint32_t g) {
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const uint32_t k = g * G + i;
+      bwd_vec<DT, GT, VLOAD, VSTORE>(dst, k, buf[i], lse, w, yv - k * uint32_t(T), slot, tid);
+    }
+  });
+  for (uint32_t k = ngroups * G; k < full_steps; ++k)
+    bwd_vec<DT, GT, VLOAD, VSTORE>(dst, k, fetch<VLOAD>(src, k), lse, w, yv - k * uint32_t(T),
+                                   slot, tid);
+  if (full_steps * uint32_t(T) < nvec) {
+    const uint32_t k = full_steps, v = k * uint32_t(T) + tid;
+    if (v < nfull) {
+      bwd_vec<DT, GT, VLOAD, VSTORE>(dst, k, fetch<VLOAD>(src, k), lse, w, yv - k * uint32_t(T),
+                                     slot, tid);
+    } else if (v == nfull) {
+      for (int64_t j = int64_t(v) * VEC; j < width; ++j) {
+        const float z = Elt<DT>::load1(src.row, j);
+        dst.store1(j, j == y ? w * (prob(z, lse) - 1.0f) : w * prob(z, lse));
+      }
+    }
+  }
+}
+
+template <int DT, int GT, bool ALIGNED>
+__global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(8)))
+void bwd_kernel(BwdArgs p) {
+  constexpr int VEC = Elt<DT>::VEC;
+  const int T = blockDim.x, tid = threadIdx.x;
+  for (int64_t row = blockIdx.x; row < p.n_rows; row += gridDim.x) {
+    const char* rp = p.logits + row * p.row_bytes;
+    char* gp = p.grad + row * p.grad_row_bytes;
+    const int64_t y = p.labels[row];
+    const int kind = y == p.ignore_index ? 1 : ((y < 0 || y >= p.vocab) ? 2 : 0);
+    if (kind == 2 && tid == 0 && p.status_flag) atomicOr(p.status_flag, BI_FLAG_BAD_LABEL);
+    const float lse = kind == 0 ? p.lse[row] : 0.0f;
+    const float w = (kind == 0 && p.weights) ? p.weights[row] : 1.0f;
+    const RowSrc src = row_src(rp, p.vocab * (DT == BI_BF16 ? 2 : 4), T, tid);
+    const RowDst<GT, VEC> dst(gp, p.vocab * (GT == BI_BF16 ? 2 : 4), T, tid);
+    const bool vload = ALIGNED || (reinterpret_cast<uintptr_t>(rp) & 3u) == 0;
+    const bool vstore = ALIGNED || (reinterpret_cast<uintptr_t>(gp) & 3u) == 0;
+    if (ALIGNED || (vload && vstore)) {
+      bwd_row<DT, GT, true, true>(p, src, dst, y, kind, lse, w, T, tid);
+    } else if (vload) {
+      bwd_row<DT, GT, true, false>(p, src, dst, y, kind, lse, w, T, tid);
+    } else if (vstore) {
+      bwd_row<DT, GT, false, true>(p, src, dst, y, kind, lse, w, T, tid);
+    } else {
+      bwd_row<DT, GT, false, false>(p, src, dst, y, kind, lse, w, T, tid);
+    }
+  }
+}
+
+// One thread per row; chunks in ascending order (natural units).
+__global__ __launch_bounds__(256) void combine_kernel(const bi_stats* stats, int64_t n_chunks,
+                                                      int64_t n_rows, const int64_t* labels,
+                                                      int64_t ignore_index, float* logprob,
+                                                      float* entropy, float* lse_out) {
+  const int64_t row = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (row >= n_rows) return;
+  float M = -INFINITY;
+  for (int64_t c = 0; c < n_chunks; ++c) M = fmaxf(M, stats[c * n_rows + row].max);
+  float S = 0.0f, U = 0.0f, t = 0.0f;
+  for (int64_t c = 0; c < n_chunks; ++c) {
+    const bi_stats s = stats[c * n_rows + row];
+    t += s.target;
+    if (s.sumexp > 0.0f) {
+      const float gap = s.max - M;
+      const float a = exp2_hw(gap * kLog2e);
+      S = fmaf(a, s.sumexp, S);
+      U = fmaf(a, fmaf(gap, s.sumexp, s.sumexp_logit), U);
+    } else if (!(s.sumexp == 0.0f)) {   // NaN statistics propagate
+      S = NAN;
+    }
+  }
+  const float lnS = kLn2 * log2_hw(S);
+  const float lse = S == 0.0f ? -INFINITY : M + lnS;
+  const int64_t y = labels[row];
+  if (lse_out) lse_out[row] = lse;
+  if (entropy) entropy[row] = lnS - U / S;
+  if (logprob) logprob[row] = y == ignore_index ? 0.0f : t - lse;
+}
+
+// ------------------------------------------------------------- host side
+
+thread_local char g_err[512];
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = 0;
+  return BI_OK;
+}
+
+size_t elem_size(int dt) { return dt == BI_BF16 ? 2 : 4; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_dtype(int dt, const char* what) {
+  if (dt != BI_F32 && dt != BI_BF16) return fail(BI_ERR_DTYPE, "%s: unknown dtype %d", what, dt);
+  return BI_OK;
+}
+
+unsigned grid_for(int64_t n_rows) {
+  const int64_t cap = int64_t(1) << 30;
+  return unsigned(n_rows < cap ? n_rows : cap);
+}
+
+int launched(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(BI_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+// every row of a [n_rows, row_bytes] array starting at p is 4-byte aligned
+bool rows_dword_aligned(const void* p, int64_t row_bytes) {
+  return aligned(p, 4) && (row_bytes % 4) == 0;
+}
+
+template <int DT, int MODE>
+void launch_fwd(const FwdArgs& a, int threads, hipStream_t s) {
+  const dim3 grid(grid_for(a.n_rows)), block(threads);
+  if (DT == BI_F32 || rows_dword_aligned(a.logits, a.row_bytes))
+    hipLaunchKernelGGL((fwd_kernel<DT, MODE, true>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((fwd_kernel<DT, MODE, false>), grid, block, 0, s, a);
+}
+
+template <int DT, int GT>
+void launch_bwd(const BwdArgs& a, int threads, hipStream_t s) {
+  const dim3 grid(grid_for(a.n_rows)), block(threads);
+  if (rows_dword_aligned(a.logits, a.row_bytes) && rows_dword_aligned(a.grad, a.grad_row_bytes))
+    hipLaunchKernelGGL((bwd_kernel<DT, GT, true>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((bwd_kernel<DT, GT, false>), grid, block, 0, s, a);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* bi_status_string(int status) {
+  switch (status) {
+    case BI_OK: return "BI_OK";
+    case BI_ERR_NULL: return "BI_ERR_NULL: a required pointer is NULL";
+    case BI_ERR_SHAPE: return "BI_ERR_SHAPE: bad size, stride, vocabulary size or offset";
+    case BI_ERR_DTYPE: return "BI_ERR_DTYPE: unknown or unsupported dtype";
+    case BI_ERR_ALIGN: return "BI_ERR_ALIGN: pointer not aligned to its element size";
+    case BI_ERR_LAUNCH: return "BI_ERR_LAUNCH: HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+const char* bi_last_error(void) { return g_err; }
+
+int bi_row_geometry(int dtype, int64_t width, int* threads, int* elems_per_load,
+                    int* loads_per_group) {
+  if (int r = check_dtype(dtype, "bi_row_geometry")) return r;
+  if (width < 1 || width >= kMaxWidth) return fail(BI_ERR_SHAPE, "bi_row_geometry: width %lld", (long long)width);
+  const Geometry g = row_geometry(dtype, width);
+  if (threads) *threads = g.threads;
+  if (elems_per_load) *elems_per_load = g.vec;
+  if (loads_per_group) *loads_per_group = g.group;
+  return ok();
+}
+
+int bi_logprob_fwd(const void* logits, int dtype, int64_t n_rows, int64_t vocab,
+                   int64_t row_stride, const int64_t* labels, int64_t ignore_index,
+                   float* logprob, float* entropy, float* lse, int32_t* status_flag,
+                   bi_stream_t stream) {
+  const char* fn = "bi_logprob_fwd";
+  if (int r = check_dtype(dtype, fn)) return r;
+  if (n_rows < 0) return fail(BI_ERR_SHAPE, "%s: n_rows %lld < 0", fn, (long long)n_rows);
+  if (vocab < 1 || vocab >= kMaxWidth)
+    return fail(BI_ERR_SHAPE, "%s: vocab %lld outside [1, 2^29)", fn, (long long)vocab);
+  if (row_stride < vocab)
+    return fail(BI_ERR_SHAPE, "%s: row_stride %lld < vocab %lld", fn, (long long)row_stride, (long long)vocab);
+  if (n_rows == 0) return ok();
+  if (!logits || !labels) return fail(BI_ERR_NULL, "%s: logits and labels are required", fn);
+  if (!logprob && !entropy && !lse) return fail(BI_ERR_NULL, "%s: no output requested", fn);
+  if (!aligned(logits, elem_size(dtype)) || !aligned(labels, 8) || !aligned(logprob, 4) ||
+      !aligned(entropy, 4) || !aligned(lse, 4) || !aligned(status_flag, 4))
+    return fail(BI_ERR_ALIGN, "%s: misaligned pointer", fn);
+  FwdArgs a{static_cast<const char*>(logits), n_rows, vocab, row_stride * int64_t(elem_size(dtype)),
+            vocab, 0, labels, ignore_index, logprob, entropy, lse, nullptr, status_flag};
+  const Geometry g = row_geometry(dtype, vocab);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == BI_BF16) launch_fwd<BI_BF16, kFull>(a, g.threads, s);
+  else launch_fwd<BI_F32, kFull>(a, g.threads, s);
+  return launched(fn);
+}
+
+int bi_vocab_chunk_stats(const void* logits_chunk, int dtype, int64_t n_rows,
+                         int64_t chunk_width, int64_t row_stride, int64_t vocab_offset,
+                         int64_t vocab, const int64_t* labels, int64_t ignore_index,
+                         bi_stats* stats, int32_t* status_flag, bi_stream_t stream) {
+  const char* fn = "bi_vocab_chunk_stats";
+  if (int r = check_dtype(dtype, fn)) return r;
+  if (n_rows < 0) return fail(BI_ERR_SHAPE, "%s: n_rows %lld < 0", fn, (long long)n_rows);
+  if (vocab < 1 || vocab >= kMaxWidth)
+    return fail(BI_ERR_SHAPE,
+                "%s: the global vocabulary size is required (got %lld); it must lie in [1, 2^29)",
+                fn, (long long)vocab);
+  if (chunk_width < 1 || vocab_offset < 0 || vocab_offset + chunk_width > vocab)
+    return fail(BI_ERR_SHAPE, "%s: chunk [%lld, %lld) outside the vocabulary [0, %lld)", fn,
+                (long long)vocab_offset, (long long)(vocab_offset + chunk_width), (long long)vocab);
+  if (row_stride < chunk_width)
+    return fail(BI_ERR_SHAPE, "%s: row_stride %lld < chunk_width %lld", fn, (long long)row_stride,
+                (long long)chunk_width);
+  if (n_rows == 0) return ok();
+  if (!logits_chunk || !labels || !stats) return fail(BI_ERR_NULL, "%s: logits, labels and stats are required", fn);
+  if (!aligned(logits_chunk, elem_size(dtype)) || !aligned(labels, 8) || !aligned(stats, 4) ||
+      !aligned(status_flag, 4))
+    return fail(BI_ERR_ALIGN, "%s: misaligned pointer", fn);
+  FwdArgs a{static_cast<const char*>(logits_chunk), n_rows, chunk_width,
+            row_stride * int64_t(elem_size(dtype)), vocab, vocab_offset, labels, ignore_index,
+            nullptr, nullptr, nullptr, stats, status_flag};
+  const Geometry g = row_geometry(dtype, chunk_width);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == BI_BF16) launch_fwd<BI_BF16, kChunk>(a, g.threads, s);
+  else launch_fwd<BI_F32, kChunk>(a, g.threads, s);
+  return launched(fn);
+}
+
+int bi_logprob_bwd(const void* logits, int dtype, int64_t n_rows, int64_t vocab,
+                   int64_t row_stride, const int64_t* labels, int64_t ignore_index,
+                   const float* lse, const float* weights, void* grad, int grad_dtype,
+                   int64_t grad_row_stride, int32_t* status_flag, bi_stream_t stream) {
+  const char* fn = "bi_logprob_bwd";
+  if (int r = check_dtype(dtype, fn)) return r;
+  if (int r = check_dtype(grad_dtype, fn)) return r;
+  if (dtype == BI_F32 && grad_dtype == BI_BF16)
+    return fail(BI_ERR_DTYPE, "%s: fp32 logits with a bf16 gradient are not supported", fn);
+  if (n_rows < 0) return fail(BI_ERR_SHAPE, "%s: n_rows %lld < 0", fn, (long long)n_rows);
+  if (vocab < 1 || vocab >= kMaxWidth)
+    return fail(BI_ERR_SHAPE, "%s: vocab %lld outside [1, 2^29)", fn, (long long)vocab);
+  if (row_stride < vocab || grad_row_stride < vocab)
+    return fail(BI_ERR_SHAPE, "%s: row strides (%lld, %lld) must be >= vocab %lld", fn,
+                (long long)row_stride, (long long)grad_row_stride, (long long)vocab);
+  if (n_rows == 0) return ok();
+  if (!logits || !labels || !lse || !grad)
+    return fail(BI_ERR_NULL, "%s: logits, labels, lse and grad are required", fn);
+  if (!aligned(logits, elem_size(dtype)) || !aligned(grad, elem_size(grad_dtype)) ||
+      !aligned(labels, 8) || !aligned(lse, 4) || !aligned(weights, 4) || !aligned(status_flag, 4))
+    return fail(BI_ERR_ALIGN, "%s: misaligned pointer", fn);
+  BwdArgs a{static_cast<const char*>(logits), static_cast<char*>(grad), n_rows, vocab,
+            row_stride * int64_t(elem_size(dtype)), grad_row_stride * int64_t(elem_size(grad_dtype)),
+            labels, ignore_index, lse, weights, status_flag};
+  const Geometry g = row_geometry(dtype, vocab);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == BI_BF16 && grad_dtype == BI_BF16) launch_bwd<BI_BF16, BI_BF16>(a, g.threads, s);
+  else if (dtype == BI_BF16) launch_bwd<BI_BF16, BI_F32>(a, g.threads, s);
+  else launch_bwd<BI_F32, BI_F32>(a, g.threads, s);
+  return launched(fn);
+}
+
+int bi_stats_combine(const bi_stats* stats, int64_t n_chunks, int64_t n_rows,
+                     const int64_t* labels, int64_t ignore_index, float* logprob,
+                     float* entropy, float* lse, bi_stream_t stream) {
+  const char* fn = "bi_stats_combine";
+  if (n_chunks < 1) return fail(BI_ERR_SHAPE, "%s: n_chunks %lld < 1", fn, (long long)n_chunks);
+  if (n_rows < 0) return fail(BI_ERR_SHAPE, "%s: n_rows %lld < 0", fn, (long long)n_rows);
+  if (n_rows == 0) return ok();
+  if (!stats || !labels) return fail(BI_ERR_NULL, "%s: stats and labels are required", fn);
+  if (!logprob && !entropy && !lse) return fail(BI_ERR_NULL, "%s: no output requested", fn);
+  if (!aligned(stats, 4) || !aligned(labels, 8) || !aligned(logprob, 4) || !aligned(entropy, 4) ||
+      !aligned(lse, 4))
+    return fail(BI_ERR_ALIGN, "%s: misaligned pointer", fn);
+  const unsigned threads = 256;
+  const int64_t blocks = (n_rows + threads - 1) / threads;
+  if (blocks > 0x7fffffff) return fail(BI_ERR_SHAPE, "%s: too many rows", fn);
+  hipLaunchKernelGGL(combine_kernel, dim3(unsigned(blocks)), dim3(threads), 0,
+                     static_cast<hipStream_t>(stream), stats, n_chunks, n_rows, labels,
+                     ignore_index, logprob, entropy, lse);
+  return launched(fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,194 @@
+/*
+ * bi_logprob.h - batch-invariant per-token logprob, entropy and gradient over a
+ * large vocabulary, for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  For row i of a logits matrix z [n_rows, vocab] (bf16 or
+ * fp32, -inf allowed for masked columns), its label y_i and an optional weight
+ * w_i, with m = max_j z_j and F = { j : z_j > -inf }:
+ *
+ *   lse      = m + ln sum_{j in F} exp(z_j - m)
+ *   logprob  = z_y - lse                    (+0.0 when y == ignore_index)
+ *   entropy  = lse - sum_{j in F} p_j z_j = -sum_{j in F} p_j ln p_j
+ *   grad_j   = w * (p_j - [j == y]),   p_j = exp(z_j - lse)
+ *
+ * Sources (page titles and sections):
+ *  - "[RL] Avoid full-vocab gather for TP policy statistics" (torchtitan PR
+ *    #4685), Summary and Why: token logprobs and entropy from per-token
+ *    sufficient statistics (global maximum, softmax denominator, target
+ *    contribution, entropy-weighted sum); entropy is a metric without a
+ *    gradient; the per-token gradient comes from the cross-entropy backward.
+ *  - same page, Correctness and compatibility: ignored labels, partially
+ *    masked logits, non-uniformly weighted gradients, FP32/BF16, even and
+ *    uneven vocabulary sizes.
+ *  - same page, review reply "Input sharding contract of compute_logprobs":
+ *    full-row calls take [N, V] logits; the vocabulary-parallel path takes the
+ *    local shard [T, V_local] and needs the global vocabulary size.
+ *  - same page, review reply "Batch invariance under the patched logprob
+ *    path", Q1/Q2: a trainer and a generator agree bit for bit only when they
+ *    use the same operation sequence and summation grouping; the maximum
+ *    combines exactly across shards, sums do not.
+ *  - "torchtitan-batch-invarient-GDN" (README), intro and Result: the goal is
+ *    the trainer's recomputed logprob matching the generator's bit for bit.
+ *
+ * Batch invariance.  Each row is reduced by one workgroup whose size, vector
+ * width, column-to-lane map and reduction tree are functions of (dtype, width)
+ * only - never of n_rows, the grid, the device or the row's alignment.  Every
+ * row's outputs are therefore bit-identical whatever batch it sits in.  The
+ * chunked path (bi_vocab_chunk_stats + bi_stats_combine) is exact in real
+ * arithmetic but is NOT bitwise equal to bi_logprob_fwd; callers that need
+ * trainer/generator bit equality use bi_logprob_fwd on full rows.
+ *
+ * Conventions for every entry point.
+ *  - Array arguments are DEVICE pointers; the caller owns every buffer and
+ *    keeps it alive until the work queued on `stream` has finished.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream).  They never synchronize and never allocate.
+ *  - Arguments are validated on the host before anything is queued; on any
+ *    error nothing is launched and a bi_status code is returned.  The reason
+ *    is also kept, per thread, for bi_last_error().
+ *  - Logits are row-major with a row pitch of `row_stride` elements
+ *    (row_stride >= width); the last dimension is contiguous.  Pointers must be
+ *    aligned to their element size; rows need not be 16-byte aligned.
+ *  - Labels are int64.  A label that is neither ignore_index nor in
+ *    [0, vocab) cannot be checked on the host without a sync: the kernels OR
+ *    BI_FLAG_BAD_LABEL into *status_flag (when non-NULL) and write NaN for that
+ *    row's logprob and gradient row.
+ *  - logprob, entropy and lse are always fp32.
+ */
+#ifndef BI_LOGPROB_H
+#define BI_LOGPROB_H
+
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define BI_API __attribute__((visibility("default")))
+#else
+#define BI_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types of logits and gradients. */
+enum { BI_F32 = 0, BI_BF16 = 1 };
+
+/* Status codes returned by every entry point. */
+enum {
+  BI_OK = 0,
+  BI_ERR_NULL = 1,   /* a required pointer is NULL */
+  BI_ERR_SHAPE = 2,  /* bad size, stride, vocabulary size or offset */
+  BI_ERR_DTYPE = 3,  /* unknown dtype or unsupported (logits, grad) pair */
+  BI_ERR_ALIGN = 4,  /* a pointer is not aligned to its element size */
+  BI_ERR_LAUNCH = 5  /* the HIP launch failed (see bi_last_error) */
+};
+
+/* Bits ORed into *status_flag by the kernels. */
+enum { BI_FLAG_BAD_LABEL = 1 };
+
+typedef void* bi_stream_t; /* a hipStream_t */
+
+/* Per-(chunk, row) sufficient statistics, 16 bytes.
+ *   max          m_c = max of the chunk's logits (-inf if all are -inf)
+ *   sumexp       S_c = sum over finite columns of exp(z - m_c)
+ *   target       z_y if the label lies in this chunk, else 0.0 (NaN for a bad
+ *                label), so that summing over chunks yields z_y
+ *   sumexp_logit U_c = sum over finite columns of exp(z - m_c) * (z - m_c);
+ *                the unshifted sum of exp(z - m_c) * z is U_c + m_c * S_c
+ * A fully masked chunk has (max, sumexp, sumexp_logit) = (-inf, 0, 0). */
+typedef struct {
+  float max;
+  float sumexp;
+  float target;
+  float sumexp_logit;
+} bi_stats;
+
+/* Forward over full rows: logprob, entropy and lse per row.
+ * Defined in PR #4685 (Summary, Why) and its reply "Input sharding contract of
+ * compute_logprobs" (full [N, V] logits; logprob = -cross_entropy, reduction
+ * "none").  This is the batch-invariant path.
+ *   logits       [n_rows, row_stride] of dtype (BI_F32 or BI_BF16); columns
+ *                [0, vocab) are read
+ *   n_rows       >= 0; 0 is a no-op
+ *   vocab        1 <= vocab < 2^29
+ *   row_stride   >= vocab, in elements
+ *   labels       [n_rows] int64
+ *   ignore_index label value of ignored rows (-100 in the pages' setting);
+ *                such rows get logprob +0.0 and still get entropy and lse
+ *   logprob, entropy, lse  [n_rows] fp32 each; any may be NULL, not all
+ *   status_flag  optional device int32, see BI_FLAG_BAD_LABEL
+ */
+BI_API int bi_logprob_fwd(const void* logits, int dtype, int64_t n_rows, int64_t vocab,
+                   int64_t row_stride, const int64_t* labels, int64_t ignore_index,
+                   float* logprob, float* entropy, float* lse,
+                   int32_t* status_flag, bi_stream_t stream);
+
+/* Backward: grad = w * (softmax - onehot(label)) from the saved lse.
+ * Defined in PR #4685 (Summary: reuse the cross-entropy backward for
+ * per-token gradients; Correctness and compatibility: non-uniformly weighted
+ * gradients; the review's backward returns only the logits gradient).
+ *   lse          [n_rows] fp32, from bi_logprob_fwd or bi_stats_combine
+ *   weights      [n_rows] fp32 per-token weights, NULL means 1.  For a loss
+ *                L = sum_i w_i * CE_i = -sum_i w_i * logprob_i, pass
+ *                w_i = -dL/dlogprob_i.
+ *   grad         [n_rows, grad_row_stride] of grad_dtype; columns [0, vocab)
+ *                are written.  Ignored rows are written +0.0 without reading
+ *                their logits.  Masked (-inf) columns get +0.0.
+ *   (dtype, grad_dtype) must be (F32, F32), (BF16, BF16) or (BF16, F32);
+ *   a bf16 gradient is the fp32 value rounded to nearest even.
+ *   grad_row_stride >= vocab.
+ */
+BI_API int bi_logprob_bwd(const void* logits, int dtype, int64_t n_rows, int64_t vocab,
+                   int64_t row_stride, const int64_t* labels, int64_t ignore_index,
+                   const float* lse, const float* weights,
+                   void* grad, int grad_dtype, int64_t grad_row_stride,
+                   int32_t* status_flag, bi_stream_t stream);
+
+/* Statistics of one vocabulary chunk: global columns
+ * [vocab_offset, vocab_offset + chunk_width) held as a [n_rows, chunk_width]
+ * view.  Defined in PR #4685, Why (shard-local sufficient statistics) and the
+ * reply "Input sharding contract of compute_logprobs" (the vocabulary-parallel
+ * path takes the local shard and requires the global vocabulary size; without
+ * it the call fails).
+ *   logits_chunk  points at global column vocab_offset of row 0
+ *   chunk_width   >= 1; vocab_offset >= 0; vocab_offset + chunk_width <= vocab
+ *   vocab         the global vocabulary size (labels are global columns)
+ *   stats         [n_rows] bi_stats for this chunk
+ */
+BI_API int bi_vocab_chunk_stats(const void* logits_chunk, int dtype, int64_t n_rows,
+                         int64_t chunk_width, int64_t row_stride,
+                         int64_t vocab_offset, int64_t vocab,
+                         const int64_t* labels, int64_t ignore_index,
+                         bi_stats* stats, int32_t* status_flag, bi_stream_t stream);
+
+/* Exact combine of chunk statistics, chunks taken in ascending order.
+ * Defined in PR #4685, Why, and the reply "Batch invariance under the
+ * patched logprob path", Q2: M = max_c m_c is exact; then, for c = 0, 1, ...,
+ * S += e^(m_c - M) S_c, U += e^(m_c - M) (U_c + (m_c - M) S_c), t += t_c;
+ * a chunk with S_c == 0 contributes nothing.  lse = M + ln S,
+ * logprob = t - lse (+0.0 if ignored), entropy = ln S - U / S.
+ *   stats    [n_chunks][n_rows] bi_stats (chunk-major)
+ *   n_chunks >= 1
+ *   logprob, entropy, lse  [n_rows] fp32 each; any may be NULL, not all
+ */
+BI_API int bi_stats_combine(const bi_stats* stats, int64_t n_chunks, int64_t n_rows,
+                     const int64_t* labels, int64_t ignore_index,
+                     float* logprob, float* entropy, float* lse, bi_stream_t stream);
+
+/* Human-readable name of a status code (static string). */
+BI_API const char* bi_status_string(int status);
+
+/* Detail of the last error returned on this thread ("" if none). */
+BI_API const char* bi_last_error(void);
+
+/* The launch geometry used for rows of `width` columns of `dtype`: threads per
+ * workgroup, elements per 128-bit load and loads per rescale group.  It is a
+ * function of (dtype, width) only; this is the batch-invariance contract. */
+BI_API int bi_row_geometry(int dtype, int64_t width, int* threads, int* elems_per_load,
+                    int* loads_per_group);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BI_LOGPROB_H */

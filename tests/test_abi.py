@@ -1,0 +1,145 @@
+"""The C ABI on the host: the library loads, exports every declared symbol, and
+rejects bad arguments with the documented status before touching the device.
+
+These run without a GPU: every call here fails validation on the host, so no
+HIP work is ever queued.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import entropy_bi_logprob_amd as bi
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "bi_logprob.h")
+
+P = ctypes.c_void_p(0x10000)      # a well-aligned stand-in pointer, never dereferenced
+P2 = ctypes.c_void_p(0x10002)     # 2-byte aligned
+NUL = None
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(bi.library_path()):
+        pytest.skip("library not built")
+    return bi.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"BI_API\s+[\w\s\*]+?\b(bi_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_four_entry_points():
+    names = declared_functions()
+    for fn in ("bi_logprob_fwd", "bi_logprob_bwd", "bi_vocab_chunk_stats", "bi_stats_combine"):
+        assert fn in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    for fn in declared_functions():
+        assert hasattr(L, fn), fn
+
+
+def test_status_strings(L):
+    for code in range(6):
+        assert L.bi_status_string(code)
+    assert b"unknown" in L.bi_status_string(99)
+
+
+def fwd(L, logits=P, dtype=bi.BI_BF16, n=4, v=100, rs=100, labels=P, ign=-100,
+        lp=P, ent=P, lse=P, flag=NUL):
+    return L.bi_logprob_fwd(logits, dtype, n, v, rs, labels, ign, lp, ent, lse, flag, NUL)
+
+
+def test_fwd_argument_errors(L):
+    assert fwd(L, dtype=7) == bi.BI_ERR_DTYPE
+    assert fwd(L, n=-1) == bi.BI_ERR_SHAPE
+    assert fwd(L, v=0) == bi.BI_ERR_SHAPE
+    assert fwd(L, v=1 << 29, rs=1 << 29) == bi.BI_ERR_SHAPE
+    assert fwd(L, rs=99) == bi.BI_ERR_SHAPE
+    assert fwd(L, logits=NUL) == bi.BI_ERR_NULL
+    assert fwd(L, labels=NUL) == bi.BI_ERR_NULL
+    assert fwd(L, lp=NUL, ent=NUL, lse=NUL) == bi.BI_ERR_NULL
+    assert fwd(L, logits=P2, dtype=bi.BI_F32) == bi.BI_ERR_ALIGN
+    assert fwd(L, labels=ctypes.c_void_p(0x10004)) == bi.BI_ERR_ALIGN
+    assert fwd(L, lp=ctypes.c_void_p(0x10001)) == bi.BI_ERR_ALIGN
+    assert fwd(L, rs=99) == bi.BI_ERR_SHAPE
+    assert b"row_stride" in L.bi_last_error()
+
+
+def test_fwd_empty_batch_is_a_no_op(L):
+    # n_rows == 0 succeeds even with NULL buffers and queues nothing
+    assert fwd(L, n=0, logits=NUL, labels=NUL, lp=NUL, ent=NUL, lse=NUL) == bi.BI_OK
+    assert L.bi_last_error() == b""
+
+
+def bwd(L, logits=P, dtype=bi.BI_BF16, n=4, v=100, rs=100, labels=P, ign=-100, lse=P,
+        w=NUL, grad=P, gdt=bi.BI_BF16, grs=100, flag=NUL):
+    return L.bi_logprob_bwd(logits, dtype, n, v, rs, labels, ign, lse, w, grad, gdt, grs, flag, NUL)
+
+
+def test_bwd_argument_errors(L):
+    assert bwd(L, dtype=bi.BI_F32, gdt=bi.BI_BF16) == bi.BI_ERR_DTYPE
+    assert bwd(L, gdt=5) == bi.BI_ERR_DTYPE
+    assert bwd(L, grs=50) == bi.BI_ERR_SHAPE
+    assert bwd(L, lse=NUL) == bi.BI_ERR_NULL
+    assert bwd(L, grad=NUL) == bi.BI_ERR_NULL
+    assert bwd(L, grad=P2, gdt=bi.BI_F32) == bi.BI_ERR_ALIGN
+    assert bwd(L, w=ctypes.c_void_p(0x10002)) == bi.BI_ERR_ALIGN
+    assert bwd(L, n=0, logits=NUL, labels=NUL, lse=NUL, grad=NUL) == bi.BI_OK
+
+
+def chunk(L, logits=P, dtype=bi.BI_BF16, n=4, w=25, rs=100, off=25, v=100, labels=P,
+          stats=P, flag=NUL):
+    return L.bi_vocab_chunk_stats(logits, dtype, n, w, rs, off, v, labels, -100, stats, flag, NUL)
+
+
+def test_chunk_requires_the_global_vocabulary(L):
+    # the vocabulary-parallel path needs the global vocabulary size
+    assert chunk(L, v=0) == bi.BI_ERR_SHAPE
+    assert b"global vocabulary size is required" in L.bi_last_error()
+    assert chunk(L, off=-1) == bi.BI_ERR_SHAPE
+    assert chunk(L, off=80) == bi.BI_ERR_SHAPE        # 80 + 25 > 100
+    assert chunk(L, w=0) == bi.BI_ERR_SHAPE
+    assert chunk(L, rs=20) == bi.BI_ERR_SHAPE
+    assert chunk(L, stats=NUL) == bi.BI_ERR_NULL
+    assert chunk(L, stats=ctypes.c_void_p(0x10002)) == bi.BI_ERR_ALIGN
+
+
+def test_combine_argument_errors(L):
+    f = L.bi_stats_combine
+    assert f(P, 0, 4, P, -100, P, P, P, NUL) == bi.BI_ERR_SHAPE
+    assert f(P, 2, -1, P, -100, P, P, P, NUL) == bi.BI_ERR_SHAPE
+    assert f(NUL, 2, 4, P, -100, P, P, P, NUL) == bi.BI_ERR_NULL
+    assert f(P, 2, 4, P, -100, NUL, NUL, NUL, NUL) == bi.BI_ERR_NULL
+    assert f(P, 2, 0, NUL, -100, NUL, NUL, NUL, NUL) == bi.BI_OK
+
+
+def test_geometry_depends_on_dtype_and_width_only(L):
+    def geo(dt, w):
+        a, b, c = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+        assert L.bi_row_geometry(dt, w, ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)) == 0
+        return a.value, b.value, c.value
+
+    assert geo(bi.BI_BF16, 151_936) == (1024, 8, 2)
+    assert geo(bi.BI_F32, 151_936) == (1024, 4, 4)
+    assert geo(bi.BI_F32, 151_937) == (1024, 4, 4)
+    assert geo(bi.BI_BF16, 37_984)[1:] == (8, 2)
+    assert geo(bi.BI_BF16, 16)[0] == 64
+    for w in (1, 7, 100, 5000, 151_936):
+        t, vec, grp = geo(bi.BI_BF16, w)
+        assert t % 64 == 0 and 64 <= t <= 1024 and vec * grp == 16
+    assert L.bi_row_geometry(bi.BI_BF16, 0, None, None, None) == bi.BI_ERR_SHAPE
+
+
+def test_python_binding_rejects_host_tensors():
+    import torch
+    x = torch.zeros(2, 10, dtype=torch.bfloat16)
+    y = torch.zeros(2, dtype=torch.int64)
+    with pytest.raises(ValueError):
+        bi.fwd(x, y)
+    with pytest.raises(ValueError):
+        bi.vocab_chunk_stats(x, y, 0, None)

@@ -1,0 +1,209 @@
+"""GPU parity on small and medium shapes: the HIP path (through the C ABI)
+against the fp64 oracle, element by element.
+
+Shapes span one and many workgroup tiles, ragged last vectors and steps, odd
+widths, row strides that leave rows 2- or 4-byte aligned, ignored labels,
+masked (-inf) logits, non-uniform weights, and the degenerate V = 1 and N = 0.
+
+Tolerances (|delta| against fp64): fp32 logits 2e-4 logprob, 2e-4 entropy,
+1e-5 grad; bf16 logits 5e-3, 5e-3, 1e-3 (fp32 gradient).  A bf16 gradient must
+equal the fp32 gradient rounded to nearest even, bit for bit, and lie within
+1e-3 + half a bf16 ulp of the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import entropy_bi_logprob_amd as bi
+import oracle.bi_oracle as orc
+from golden_cases import load as load_golden
+from gpu_util import TOL, assert_close, dev, dev_logits, host, ulp_bf16
+from workloads import f32_to_bf16_bits, random_batch
+
+pytestmark = pytest.mark.gpu
+
+WIDTHS = [1, 2, 3, 7, 8, 9, 15, 16, 17, 63, 64, 65, 127, 513, 1000, 4097, 8192, 16_389,
+          65_539, 151_936, 151_937]
+
+
+def run_all(b, grad_dtypes=("f32",)):
+    logits = dev_logits(b.logits, b.dtype)
+    labels = dev(b.labels)
+    w = dev(b.weights)
+    lp, ent, lse = bi.fwd(logits, labels)
+    grads = {}
+    for gd in grad_dtypes:
+        tdt = torch.float32 if gd == "f32" else torch.bfloat16
+        grads[gd] = bi.bwd(logits, labels, lse, w, tdt)
+    torch.cuda.synchronize()
+    return (host(lp), host(ent), host(lse)), {k: host(v) for k, v in grads.items()}
+
+
+def check_against_oracle(b, outs, grads):
+    tl, te, tg = TOL[b.dtype]
+    z = orc.decode(b.logits, b.dtype)
+    olp, oent, olse = orc.forward(z, b.labels)
+    lp, ent, lse = outs
+    assert_close(lp, olp, tl, "logprob")
+    assert_close(ent, oent, te, "entropy")
+    assert_close(lse, olse, tl, "lse")
+    ign = b.labels == -100
+    assert np.all(lp[ign] == 0) and not np.any(np.signbit(lp[ign])), "ignored logprob not +0.0"
+    og = orc.backward(z, b.labels, olse, b.weights)
+    if "f32" in grads:
+        g = grads["f32"]
+        assert_close(g, og, tg, "grad")
+        assert np.all(g[ign] == 0) and not np.any(np.signbit(g[ign])), "ignored grad not +0.0"
+        if "bf16" in grads:
+            gb = grads["bf16"]
+            np.testing.assert_array_equal(gb, f32_to_bf16_bits(g))     # RNE of the fp32 path
+            gbv = orc.decode(gb, "bf16")
+            bound = tg + 0.5 * ulp_bf16(og)
+            assert np.all(np.abs(gbv - og) <= bound), "bf16 grad outside 1e-3 + ulp/2"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("V", WIDTHS)
+def test_widths(dtype, V):
+    rows = 6 if V > 60_000 else 19
+    b = random_batch(rows, V, dtype, seed=V, ignore_frac=0.2,
+                     mask_frac=0.1 if V > 4 else 0.0)
+    gds = ("f32", "bf16") if dtype == "bf16" else ("f32",)
+    outs, grads = run_all(b, gds)
+    check_against_oracle(b, outs, grads)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_peaked_and_shifted_rows(dtype):
+    # large offsets and one dominant logit per row
+    b = random_batch(12, 50_001, dtype, seed=3, sigma=3.0)
+    x = orc.decode(b.logits, dtype).astype(np.float32)
+    x += np.float32(200.0)
+    for i, y in enumerate(b.labels):
+        x[i, y] += np.float32(25.0 if i % 2 else 9.0)
+    b.logits = f32_to_bf16_bits(x) if dtype == "bf16" else x
+    outs, grads = run_all(b)
+    check_against_oracle(b, outs, grads)
+
+
+def test_uniform_rows_closed_form():
+    V = 151_936
+    x = np.full((4, V), 1.5, dtype=np.float32)
+    labels = np.array([0, 7, V - 1, -100])
+    lp, ent, lse = (host(t) for t in bi.fwd(dev_logits(x, "f32"), dev(labels)))
+    assert np.abs(lp[:3] + np.log(V)).max() < 2e-6
+    assert np.abs(ent - np.log(V)).max() < 2e-6
+    assert np.abs(lse - (1.5 + np.log(V))).max() < 2e-6
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("pad,offset", [(0, 1), (1, 0), (3, 1), (8, 3)])
+def test_strided_and_unaligned_rows(dtype, pad, offset):
+    V, n = 20_011, 7
+    b = random_batch(n, V, dtype, seed=11 + pad, ignore_frac=0.2, mask_frac=0.05)
+    stride = V + pad
+    store = np.zeros(offset + n * stride, dtype=b.logits.dtype)
+    for i in range(n):
+        store[offset + i * stride: offset + i * stride + V] = b.logits[i]
+    base = dev_logits(store, dtype)
+    view = base[offset:offset + (n - 1) * stride + V].as_strided((n, V), (stride, 1))
+    labels, w = dev(b.labels), dev(b.weights)
+    lp, ent, lse = bi.fwd(view, labels)
+    gstore = torch.zeros(offset + n * stride, dtype=torch.float32, device="cuda")
+    gview = gstore[offset:offset + (n - 1) * stride + V].as_strided((n, V), (stride, 1))
+    bi.bwd(view, labels, lse, w, out=gview)
+    # contiguous copy: must be bit-identical (row alignment changes nothing)
+    lp2, ent2, lse2 = bi.fwd(dev_logits(b.logits, dtype), labels)
+    g2 = bi.bwd(dev_logits(b.logits, dtype), labels, lse2, w, torch.float32)
+    torch.cuda.synchronize()
+    for a, c in ((lp, lp2), (ent, ent2), (lse, lse2), (gview, g2)):
+        np.testing.assert_array_equal(host(a.contiguous()), host(c))
+    check_against_oracle(b, (host(lp), host(ent), host(lse)), {"f32": host(gview.contiguous())})
+
+
+def test_bf16_gradient_on_odd_rows_with_2_byte_alignment():
+    V, n = 3001, 5
+    b = random_batch(n, V, "bf16", seed=5, ignore_frac=0.2)
+    stride = V + 1
+    store = np.zeros(1 + n * stride, dtype=np.uint16)
+    for i in range(n):
+        store[1 + i * stride: 1 + i * stride + V] = b.logits[i]
+    base = dev_logits(store, "bf16")
+    view = base[1:1 + (n - 1) * stride + V].as_strided((n, V), (stride, 1))
+    labels, w = dev(b.labels), dev(b.weights)
+    lp, ent, lse = bi.fwd(view, labels)
+    gstore = torch.zeros(1 + n * stride, dtype=torch.bfloat16, device="cuda")
+    gview = gstore[1:1 + (n - 1) * stride + V].as_strided((n, V), (stride, 1))
+    bi.bwd(view, labels, lse, w, out=gview)
+    g32 = bi.bwd(view, labels, lse, w, torch.float32)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(gview.contiguous()), f32_to_bf16_bits(host(g32)))
+    check_against_oracle(b, (host(lp), host(ent), host(lse)), {"f32": host(g32)})
+
+
+def test_golden_tiny_rows():
+    for c in load_golden():
+        logits = dev_logits(c["logits"][None, :], c["dtype"])
+        labels = dev(np.array([c["label"]]))
+        lp, ent, lse = bi.fwd(logits, labels)
+        g = bi.bwd(logits, labels, lse, dev(np.array([c["weight"]], np.float32)), torch.float32)
+        torch.cuda.synchronize()
+        tl, te, tg = TOL[c["dtype"]]
+        assert abs(host(lp)[0] - c["logprob"]) <= tl
+        assert abs(host(ent)[0] - c["entropy"]) <= te
+        assert abs(host(lse)[0] - c["lse"]) <= tl
+        assert np.abs(host(g)[0] - np.array(c["grad"])).max() <= tg
+
+
+def test_bad_labels_raise_the_flag_and_give_nan():
+    V = 1000
+    b = random_batch(5, V, "bf16", seed=2)
+    labels = np.array([3, V, -1, -100, 10 ** 12])
+    logits, lab = dev_logits(b.logits, "bf16"), dev(labels)
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    lp, ent, lse = bi.fwd(logits, lab, status=flag)
+    g = bi.bwd(logits, lab, lse, None, torch.float32, status=flag)
+    torch.cuda.synchronize()
+    assert int(flag.item()) == bi.BI_FLAG_BAD_LABEL
+    lp, g = host(lp), host(g)
+    assert np.isfinite(lp[0]) and np.isnan(lp[1]) and np.isnan(lp[2]) and lp[3] == 0
+    assert np.isnan(lp[4]) and np.all(np.isfinite(host(ent)))
+    assert np.isnan(g[1]).all() and np.isnan(g[2]).all() and np.isnan(g[4]).all()
+    assert np.isfinite(g[0]).all() and np.all(g[3] == 0)
+    flag.zero_()
+    bi.fwd(logits[:1], lab[:1], status=flag)
+    torch.cuda.synchronize()
+    assert int(flag.item()) == 0
+
+
+def test_empty_batch_and_fully_masked_rows():
+    lp, ent, lse = bi.fwd(torch.empty((0, 10), dtype=torch.bfloat16, device="cuda"),
+                          torch.empty(0, dtype=torch.int64, device="cuda"))
+    assert lp.numel() == 0
+    x = np.full((2, 300), -np.inf, dtype=np.float32)
+    x[1, 5] = 2.0
+    lp, ent, lse = (host(t) for t in bi.fwd(dev_logits(x, "f32"), dev(np.array([1, 5]))))
+    assert lse[0] == -np.inf and np.isnan(lp[0]) and np.isnan(ent[0])
+    assert lse[1] == 2.0 and lp[1] == 0.0 and ent[1] == 0.0
+
+
+def test_nan_logits_propagate():
+    x = np.zeros((1, 5000), dtype=np.float32)
+    x[0, 1234] = np.nan
+    lp, ent, lse = (host(t) for t in bi.fwd(dev_logits(x, "f32"), dev(np.array([0]))))
+    assert np.isnan(lse[0]) and np.isnan(lp[0])
+
+
+def test_autograd_wrapper_matches_bwd():
+    b = random_batch(8, 7001, "bf16", seed=9, ignore_frac=0.25)
+    logits = dev_logits(b.logits, "bf16").requires_grad_(True)
+    labels = dev(b.labels)
+    lp, ent = bi.logprob_entropy(logits, labels)
+    adv = torch.linspace(-1.0, 2.0, 8, device="cuda")
+    (-(adv * lp).sum()).backward()
+    assert not ent.requires_grad
+    _, _, lse = bi.fwd(logits.detach(), labels)
+    g = bi.bwd(logits.detach(), labels, lse, adv.contiguous(), torch.bfloat16)
+    torch.cuda.synchronize()
+    assert logits.grad.dtype == torch.bfloat16
+    np.testing.assert_array_equal(host(logits.grad), host(g))
