@@ -62,6 +62,7 @@ constexpr int64_t kMaxWidth = int64_t(1) << 29;
 constexpr int kGroupElems = BI_GROUP_ELEMS;   // elements per lane per rescale
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 
 struct Geometry {
   int threads;  // workgroup size
@@ -499,16 +500,17 @@ __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
 
 // Where one lane writes the gradients of its vectors: vector k*T + tid holds
 // VEC values of GSIZE bytes each.  The 4-byte-aligned path uses non-temporal
-// buffer_store_dwordx4 (lane offset in a VGPR, step offset in an SGPR).
+// global_store_dwordx4 from a per-step base plus the lane's offset.  (Buffer
+// stores with an SGPR offset are avoided on purpose: for those the compiler
+// inserts no wait state before the data registers are overwritten, and on
+// gfx950 the stored data was then observed to be corrupted.)
 template <int GT, int VEC>
 struct RowDst {
   static constexpr int kBytes = VEC * (GT == BI_BF16 ? 2 : 4);   // per vector
-  __amdgpu_buffer_rsrc_t rs;
   char* row;
   uint32_t lane_off, step_bytes;
 
-  __device__ RowDst(char* r, int64_t row_bytes, int T, int tid) {
-    rs = __builtin_amdgcn_make_buffer_rsrc(r, (short)0, int(row_bytes), kRsrcWord3);
+  __device__ RowDst(char* r, int T, int tid) {
     row = r;
     lane_off = uint32_t(tid) * kBytes;
     step_bytes = uint32_t(T) * kBytes;
@@ -533,10 +535,11 @@ struct RowDst {
       }
     }
     if constexpr (VSTORE) {
+      char* base = row + k * step_bytes;
 #pragma unroll
       for (int h = 0; h < kBytes / 16; ++h)
-        __builtin_amdgcn_raw_buffer_store_b128(w[h], rs, lane_off + 16u * h, k * step_bytes,
-                                               kNonTemporal);
+        __builtin_nontemporal_store(static_cast<u32x4_a4>(w[h]),
+                                    reinterpret_cast<u32x4_a4*>(base + lane_off + 16u * h));
     } else {
       uint16_t* q = reinterpret_cast<uint16_t*>(row + k * step_bytes + lane_off);
 #pragma unroll
@@ -664,7 +667,7 @@ void bwd_kernel(BwdArgs p) {
     const float lse = kind == 0 ? p.lse[row] : 0.0f;
     const float w = (kind == 0 && p.weights) ? p.weights[row] : 1.0f;
     const RowSrc src = row_src(rp, p.vocab * (DT == BI_BF16 ? 2 : 4), T, tid);
-    const RowDst<GT, VEC> dst(gp, p.vocab * (GT == BI_BF16 ? 2 : 4), T, tid);
+    const RowDst<GT, VEC> dst(gp, T, tid);
     const bool vload = ALIGNED || (reinterpret_cast<uintptr_t>(rp) & 3u) == 0;
     const bool vstore = ALIGNED || (reinterpret_cast<uintptr_t>(gp) & 3u) == 0;
     if (ALIGNED || (vload && vstore)) {

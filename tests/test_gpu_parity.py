@@ -207,3 +207,22 @@ def test_autograd_wrapper_matches_bwd():
     torch.cuda.synchronize()
     assert logits.grad.dtype == torch.bfloat16
     np.testing.assert_array_equal(host(logits.grad), host(g))
+
+
+@pytest.mark.parametrize("V", [4097, 65_539, 147_456, 151_936, 151_937])
+@pytest.mark.parametrize("dt,gdt", [("bf16", torch.bfloat16), ("bf16", torch.float32),
+                                    ("f32", torch.float32)])
+def test_bwd_writes_every_element_deterministically(V, dt, gdt):
+    # regression: gradient stores must neither be dropped nor corrupted; the
+    # output starts as NaN (or zeros) and two runs must agree bit for bit
+    b = random_batch(6, V, dt, seed=V + 1, ignore_frac=0.2, mask_frac=0.1)
+    logits, labels, w = dev_logits(b.logits, dt), dev(b.labels), dev(b.weights)
+    lp, ent, lse = bi.fwd(logits, labels)
+    g1 = torch.full((6, V), float("nan"), dtype=gdt, device="cuda")
+    g2 = torch.zeros((6, V), dtype=gdt, device="cuda")
+    bi.bwd(logits, labels, lse, w, out=g1)
+    bi.bwd(logits, labels, lse, w, out=g2)
+    torch.cuda.synchronize()
+    assert not bool(torch.isnan(g1).any())
+    ity = torch.int16 if gdt == torch.bfloat16 else torch.int32
+    assert torch.equal(g1.view(ity), g2.view(ity))
