@@ -35,9 +35,12 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-rows", type=int, default=1024)
+    ap.add_argument("--cpu-sample-rows", type=int, default=4096)
     ap.add_argument("--profile-steps", type=int, default=None,
                     help="run only this many steps (for profilers); still prints the line")
+    ap.add_argument("--calibrate-copy-gib", type=float, default=0.0,
+                    help="first run one plain elementwise copy of this many GiB (bf16 in, "
+                         "bf16 out), a known-size reference for memory counters")
     return ap.parse_args()
 
 
@@ -48,6 +51,27 @@ def algorithmic_bytes(vocab, e_in, e_grad, chunks):
     chunk = vocab * e_in + chunks * (8 + 16)   # all chunks: logits + label + bi_stats each
     combine = chunks * 16 + 8 + 12             # stats + label + outputs
     return fwd, bwd, chunk, combine
+
+
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "large_32768x151936_bf16_hbm_traffic.md")
+KERNEL_SOURCE = os.path.join(ROOT, "entropy_bi_logprob_amd", "csrc", "bi_logprob.hip")
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed counter summary, or None when the
+    kernel source has changed since the counters were taken."""
+    import hashlib
+    import re
+
+    try:
+        text = open(TRAFFIC_SUMMARY).read()
+        block = json.loads(re.search(r"```json\n(.*?)\n```", text, re.S).group(1))
+        sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    except (OSError, AttributeError, ValueError):
+        return None
+    if block.get("source_sha256") != sha or kernel not in block.get("per_launch", {}):
+        return None
+    return block["per_launch"][kernel]["traffic_bytes"]
 
 
 def cpu_baseline(rows_total, sample_rows, seed):
@@ -135,6 +159,14 @@ def main():
         bi.bwd(logits, labels, clse, weights, out=grad, status=flag, stream=stream)
         if ev: ev[3].record(stream)
 
+    if args.calibrate_copy_gib > 0:
+        n_el = int(args.calibrate_copy_gib * (1 << 30)) // 2
+        src = torch.ones(n_el, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)            # reads n_el*2 bytes, writes n_el*2 bytes
+        torch.cuda.synchronize()
+        del src, dst
+
     steps = args.profile_steps or args.steps
     warm = 0 if args.profile_steps else args.warmup
     for _ in range(warm):
@@ -213,7 +245,7 @@ def main():
         "pct_hbm_peak": 100.0 * hbm / HBM_PEAK_GBPS,
         "roofline": {"bound": "hbm", "achieved": kernels[dom]["GBps"], "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": kernels[dom]["GBps"] / HBM_PEAK_GBPS,
-                     "traffic": None, "kernel": f"{dom} (bf16 logits, bf16 grad)",
+                     "traffic": measured_traffic(dom), "kernel": f"{dom} (bf16 logits, bf16 grad)",
                      "bytes_per_launch": kernels[dom]["bytes"]},
         "kernels": kernels,
         "chunked": chunked,

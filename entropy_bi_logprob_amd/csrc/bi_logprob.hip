@@ -132,7 +132,13 @@ struct RowSrc {
   uint32_t step_bytes;  // T * 16
 };
 
-constexpr int kNonTemporal = 2;          // cache policy bits: nt
+#ifndef BI_LOAD_POLICY
+#define BI_LOAD_POLICY 2
+#endif
+#ifndef BI_STORE_NT
+#define BI_STORE_NT 1
+#endif
+constexpr int kNonTemporal = BI_LOAD_POLICY;   // buffer-load cache policy bits (2 = nt)
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format
 
 __device__ inline RowSrc row_src(const char* row, int64_t row_bytes, int T, int tid) {
@@ -537,9 +543,11 @@ struct RowDst {
     if constexpr (VSTORE) {
       char* base = row + k * step_bytes;
 #pragma unroll
-      for (int h = 0; h < kBytes / 16; ++h)
-        __builtin_nontemporal_store(static_cast<u32x4_a4>(w[h]),
-                                    reinterpret_cast<u32x4_a4*>(base + lane_off + 16u * h));
+      for (int h = 0; h < kBytes / 16; ++h) {
+        u32x4_a4* q = reinterpret_cast<u32x4_a4*>(base + lane_off + 16u * h);
+        if constexpr (BI_STORE_NT) __builtin_nontemporal_store(static_cast<u32x4_a4>(w[h]), q);
+        else *q = w[h];
+      }
     } else {
       uint16_t* q = reinterpret_cast<uint16_t*>(row + k * step_bytes + lane_off);
 #pragma unroll
