@@ -1,12 +1,13 @@
 """Benchmark: batch-invariant per-token logprob / entropy / gradient on one MI355X.
 
 One step is one pass of the hot path over a batch of 32,768 x 151,936 bf16
-logits (64 rollouts x 512 tokens, Qwen3 vocabulary): the full-row forward
-(logprob, entropy, lse) and the backward (bf16 grad = w * (softmax - onehot)).
-The vocabulary-chunked variant of the same step (4 x bi_vocab_chunk_stats of
-37,984 columns + bi_stats_combine, then the backward) is timed in the same run
-and reported under "chunked".  Inputs are seeded synthetic logits, resident in
-HBM before the timed region.
+logits (64 rollouts x 512 tokens, Qwen3 vocabulary) with per-token weights:
+the full-row forward (logprob, entropy, lse) and the backward (bf16 grad =
+w * (softmax - onehot)), as one bi_logprob_fwd_bwd call.  The same step as two
+calls (bi_logprob_fwd + bi_logprob_bwd, "two_call") and the vocabulary-chunked
+variant (4 x bi_vocab_chunk_stats of 37,984 columns + bi_stats_combine + the
+backward, "chunked") are timed in the same run.  Inputs are seeded synthetic
+logits, resident in HBM before the timed region.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
 
@@ -141,7 +142,13 @@ def main():
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
 
-    def step_full(ev=None):
+    def step_fused(ev=None):
+        if ev: ev[0].record(stream)
+        bi.fwd_bwd(logits, labels, weights, out=(lp, ent, lse), grad=grad, status=flag,
+                   stream=stream)
+        if ev: ev[1].record(stream)
+
+    def step_two_calls(ev=None):
         if ev: ev[0].record(stream)
         bi.fwd(logits, labels, out=(lp, ent, lse), status=flag, stream=stream)
         if ev: ev[1].record(stream)
@@ -170,60 +177,57 @@ def main():
     steps = args.profile_steps or args.steps
     warm = 0 if args.profile_steps else args.warmup
     for _ in range(warm):
-        step_full()
+        step_fused()
+        step_two_calls()
         step_chunked()
     torch.cuda.synchronize()
 
-    # timed region: K full-row steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(steps):
-        step_full(evs[k])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    t_fwd = [e[0].elapsed_time(e[1]) for e in evs]
-    t_bwd = [e[1].elapsed_time(e[2]) for e in evs]
-    ms_step = wall * 1e3 / steps
+    def timed(step, n_events):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_events)]
+               for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(steps):
+            step(evs[k])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        seg = [[e[i].elapsed_time(e[i + 1]) for e in evs] for i in range(n_events - 1)]
+        return wall * 1e3 / steps, seg
 
-    # the chunked variant of the step, same run
-    cevs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    for k in range(steps):
-        step_chunked(cevs[k])
-    torch.cuda.synchronize()
-    cwall = time.perf_counter() - t1
-    t_chunk = [e[0].elapsed_time(e[1]) for e in cevs]
-    t_comb = [e[1].elapsed_time(e[2]) for e in cevs]
-    t_cbwd = [e[2].elapsed_time(e[3]) for e in cevs]
+    # timed region: K steps of the whole path (one fused pass per row)
+    ms_step, (t_fused,) = timed(step_fused, 2)
+    # the same work as two calls, and the vocabulary-chunked variant, same run
+    ms_two, (t_fwd, t_bwd) = timed(step_two_calls, 3)
+    ms_chunked, (t_chunk, t_comb, t_cbwd) = timed(step_chunked, 4)
     assert int(flag.item()) == 0
 
     f_b, b_b, c_b, m_b = algorithmic_bytes(V, 2, 2, len(bounds))
+    fused_b = V * (2 + 2) + 8 + 4 + 12       # one read of the logits, one write of the grad
     med = lambda xs: float(np.median(xs))
     mean = lambda xs: float(np.mean(xs))
-    fwd_ms, bwd_ms = mean(t_fwd), mean(t_bwd)
-    step_bytes = N * (f_b + b_b)
     gbps = lambda nbytes, ms: nbytes / (ms * 1e-3) / 1e9
-    hbm = gbps(step_bytes, ms_step)
+    hbm = gbps(N * fused_b, ms_step)
     rows_s = N / (ms_step * 1e-3)
     kernels = {
-        "fwd": {"ms": fwd_ms, "ms_median": med(t_fwd), "GBps": gbps(N * f_b, fwd_ms),
+        "fused": {"ms": mean(t_fused), "ms_median": med(t_fused),
+                  "GBps": gbps(N * fused_b, mean(t_fused)), "bytes": N * fused_b},
+        "fwd": {"ms": mean(t_fwd), "ms_median": med(t_fwd), "GBps": gbps(N * f_b, mean(t_fwd)),
                 "bytes": N * f_b},
-        "bwd": {"ms": bwd_ms, "ms_median": med(t_bwd), "GBps": gbps(N * b_b, bwd_ms),
+        "bwd": {"ms": mean(t_bwd), "ms_median": med(t_bwd), "GBps": gbps(N * b_b, mean(t_bwd)),
                 "bytes": N * b_b},
+        "chunk_stats_x4": {"ms": mean(t_chunk), "GBps": gbps(N * c_b, mean(t_chunk)),
+                           "bytes": N * c_b},
+        "combine": {"ms": mean(t_comb), "GBps": gbps(N * m_b, mean(t_comb)), "bytes": N * m_b},
     }
     for k in kernels.values():
         k["frac_of_peak"] = k["GBps"] / HBM_PEAK_GBPS
-    dom = max(kernels, key=lambda k: kernels[k]["ms"])
-    cms = cwall * 1e3 / steps
-    chunked = {
-        "ms_per_step": cms,
-        "rows_per_s": N / (cms * 1e-3),
-        "hbm_GBps": gbps(N * (c_b + m_b + b_b), cms),
-        "chunk_stats_ms_4x": mean(t_chunk), "combine_ms": mean(t_comb), "bwd_ms": mean(t_cbwd),
-        "chunk_stats_GBps": gbps(N * c_b, mean(t_chunk)),
-    }
+    dom = "fused"
+    two_call = {"ms_per_step": ms_two, "rows_per_s": N / (ms_two * 1e-3),
+                "hbm_GBps": gbps(N * (f_b + b_b), ms_two),
+                "pct_hbm_peak": 100 * gbps(N * (f_b + b_b), ms_two) / HBM_PEAK_GBPS}
+    chunked = {"ms_per_step": ms_chunked, "rows_per_s": N / (ms_chunked * 1e-3),
+               "hbm_GBps": gbps(N * (c_b + m_b + b_b), ms_chunked),
+               "bwd_ms": mean(t_cbwd)}
     line = {
         "metric": METRIC,
         "value": rows_s,
@@ -239,15 +243,17 @@ def main():
         "data": "synthetic",
         "config": {"workload": "large_32768x151936_bf16", "rows": N, "vocab": V,
                    "logits_dtype": "bf16", "grad_dtype": "bf16",
-                   "path": "full-row fwd + bwd", "seed": seed},
+                   "path": "bi_logprob_fwd_bwd (full-row fwd + bwd, one call)", "seed": seed},
         "logits_GBps": N * V * 2 / (ms_step * 1e-3) / 1e9,
         "hbm_GBps": hbm,
         "pct_hbm_peak": 100.0 * hbm / HBM_PEAK_GBPS,
         "roofline": {"bound": "hbm", "achieved": kernels[dom]["GBps"], "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": kernels[dom]["GBps"] / HBM_PEAK_GBPS,
-                     "traffic": measured_traffic(dom), "kernel": f"{dom} (bf16 logits, bf16 grad)",
+                     "traffic": measured_traffic(dom),
+                     "kernel": "fused fwd+bwd (bf16 logits, bf16 grad)",
                      "bytes_per_launch": kernels[dom]["bytes"]},
         "kernels": kernels,
+        "two_call": two_call,
         "chunked": chunked,
         "input_gen_s": gen_s,
     }

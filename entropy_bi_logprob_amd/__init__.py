@@ -21,7 +21,7 @@ from typing import Optional, Tuple
 import torch  # first: the library then binds to the HIP runtime torch has loaded
 
 __all__ = [
-    "IGNORE_INDEX", "BiError", "fwd", "bwd", "vocab_chunk_stats", "stats_combine",
+    "IGNORE_INDEX", "BiError", "fwd", "bwd", "fwd_bwd", "vocab_chunk_stats", "stats_combine",
     "row_geometry", "LogprobEntropy", "logprob_entropy", "lib", "library_path",
 ]
 
@@ -77,11 +77,13 @@ def lib() -> ctypes.CDLL:
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     L.bi_logprob_fwd.argtypes = [vp, i32, i64, i64, i64, vp, i64, vp, vp, vp, vp, vp]
     L.bi_logprob_bwd.argtypes = [vp, i32, i64, i64, i64, vp, i64, vp, vp, vp, i32, i64, vp, vp]
+    L.bi_logprob_fwd_bwd.argtypes = [vp, i32, i64, i64, i64, vp, i64, vp, vp, vp, vp, vp, i32,
+                                     i64, vp, vp]
     L.bi_vocab_chunk_stats.argtypes = [vp, i32, i64, i64, i64, i64, i64, vp, i64, vp, vp, vp]
     L.bi_stats_combine.argtypes = [vp, i64, i64, vp, i64, vp, vp, vp, vp]
     L.bi_row_geometry.argtypes = [i32, i64, ctypes.POINTER(i32), ctypes.POINTER(i32),
                                   ctypes.POINTER(i32)]
-    for fn in ("bi_logprob_fwd", "bi_logprob_bwd", "bi_vocab_chunk_stats",
+    for fn in ("bi_logprob_fwd", "bi_logprob_bwd", "bi_logprob_fwd_bwd", "bi_vocab_chunk_stats",
                "bi_stats_combine", "bi_row_geometry"):
         getattr(L, fn).restype = i32
     L.bi_status_string.argtypes = [i32]
@@ -182,6 +184,33 @@ def bwd(logits: torch.Tensor, labels: torch.Tensor, lse: torch.Tensor,
         _ptr(lse), _ptr(weights), _ptr(out), _dtype_code(out.dtype), grs, _ptr(status),
         _stream(stream)))
     return out
+
+
+def fwd_bwd(logits: torch.Tensor, labels: torch.Tensor, weights: Optional[torch.Tensor] = None,
+            grad_dtype: Optional[torch.dtype] = None, ignore_index: int = IGNORE_INDEX, *,
+            out=None, grad: Optional[torch.Tensor] = None, status: Optional[torch.Tensor] = None,
+            stream=None):
+    """(logprob, entropy, lse, grad) in one pass over each row (weights known up front).
+
+    Bit-identical to ``fwd`` followed by ``bwd`` with the same weights.
+    """
+    n, v, rs = _rows(logits, "logits")
+    _vec(labels, n, torch.int64, "labels")
+    _vec(weights, n, torch.float32, "weights")
+    _vec(status, 1, torch.int32, "status")
+    if out is None:
+        out = tuple(torch.empty(n, dtype=torch.float32, device=logits.device) for _ in range(3))
+    lp, ent, lse = (_vec(o, n, torch.float32, "out") for o in out)
+    if grad is None:
+        grad = torch.empty((n, v), dtype=grad_dtype or logits.dtype, device=logits.device)
+    gn, gv, grs = _rows(grad, "grad")
+    if (gn, gv) != (n, v):
+        raise ValueError("grad must have the logits' shape")
+    _check("bi_logprob_fwd_bwd", lib().bi_logprob_fwd_bwd(
+        _ptr(logits), _dtype_code(logits.dtype), n, v, rs, _ptr(labels), ignore_index,
+        _ptr(weights), _ptr(lp), _ptr(ent), _ptr(lse), _ptr(grad), _dtype_code(grad.dtype), grs,
+        _ptr(status), _stream(stream)))
+    return lp, ent, lse, grad
 
 
 def vocab_chunk_stats(logits_chunk: torch.Tensor, labels: torch.Tensor, vocab_offset: int,

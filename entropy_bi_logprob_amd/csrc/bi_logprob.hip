@@ -57,7 +57,7 @@ constexpr int64_t kMaxWidth = int64_t(1) << 29;
 #define BI_GROUP_ELEMS 16
 #endif
 #ifndef BI_MIN_VECS_PER_LANE
-#define BI_MIN_VECS_PER_LANE 8
+#define BI_MIN_VECS_PER_LANE 32
 #endif
 constexpr int kGroupElems = BI_GROUP_ELEMS;   // elements per lane per rescale
 
@@ -151,10 +151,10 @@ __device__ inline RowSrc row_src(const char* row, int64_t row_bytes, int T, int 
   return s;
 }
 
-template <bool VLOAD>
+template <bool VLOAD, int POL = kNonTemporal>
 __device__ inline u32x4 fetch(const RowSrc& s, uint32_t k) {
   if constexpr (VLOAD) {
-    return __builtin_amdgcn_raw_buffer_load_b128(s.rs, s.lane_off, k * s.step_bytes, kNonTemporal);
+    return __builtin_amdgcn_raw_buffer_load_b128(s.rs, s.lane_off, k * s.step_bytes, POL);
   } else {
     const uint16_t* p = reinterpret_cast<const uint16_t*>(s.row + k * s.step_bytes + s.lane_off);
     u32x4 r;
@@ -262,35 +262,38 @@ __device__ inline void accumulate(Acc& a, const float* z) {
   }
 }
 
-template <int DT, int G, bool VLOAD>
+template <int DT, int G, bool VLOAD, int POL = kNonTemporal>
 __device__ inline void load_group(u32x4* buf, const RowSrc& src, uint32_t g) {
 #pragma unroll
-  for (int i = 0; i < G; ++i) buf[i] = fetch<VLOAD>(src, g * G + i);
+  for (int i = 0; i < G; ++i) buf[i] = fetch<VLOAD, POL>(src, g * G + i);
 }
 
 // Run body(buffer, g) over groups g = 0 .. n-1 of G steps each, with group
 // g+1's loads issued before group g is processed.  Two register buffers are
 // used in turn and the last group is peeled, so that every processing site
 // sees the same unconditional loads ahead of it and waits only for its own.
-template <int DT, int G, bool VLOAD, typename Body>
+// REV visits the groups from last to first (the order does not matter to an
+// elementwise body; it is used to re-read the most recently loaded data first).
+template <int DT, int G, bool VLOAD, int POL = kNonTemporal, bool REV = false, typename Body>
 __device__ inline void pipelined_groups(const RowSrc& src, uint32_t n, Body&& body) {
   if (n == 0) return;
+  auto at = [n](uint32_t g) { return REV ? n - 1 - g : g; };
   u32x4 A[G], B[G];
-  load_group<DT, G, VLOAD>(A, src, 0);
+  load_group<DT, G, VLOAD, POL>(A, src, at(0));
   for (uint32_t g = 0;;) {
     if (g + 1 == n) {
-      body(A, g);
+      body(A, at(g));
       return;
     }
-    load_group<DT, G, VLOAD>(B, src, g + 1);
-    body(A, g);
+    load_group<DT, G, VLOAD, POL>(B, src, at(g + 1));
+    body(A, at(g));
     ++g;
     if (g + 1 == n) {
-      body(B, g);
+      body(B, at(g));
       return;
     }
-    load_group<DT, G, VLOAD>(A, src, g + 1);
-    body(B, g);
+    load_group<DT, G, VLOAD, POL>(A, src, at(g + 1));
+    body(B, at(g));
     ++g;
   }
 }
@@ -307,7 +310,7 @@ __device__ inline void accumulate_group(Acc& a, const u32x4* buf) {
 // Scan one row segment of `width` columns: every lane accumulates its vectors.
 // Full groups run with the next group's loads in flight (two register
 // buffers used in turn), then single full steps, then the one ragged step.
-template <int DT, bool VLOAD>
+template <int DT, bool VLOAD, int POL = kNonTemporal>
 __device__ inline void row_scan(Acc& a, const RowSrc& src, int64_t width, int T, int tid) {
   constexpr int VEC = Elt<DT>::VEC;
   constexpr int G = kGroupElems / VEC;
@@ -316,19 +319,19 @@ __device__ inline void row_scan(Acc& a, const RowSrc& src, int64_t width, int T,
   const uint32_t full_steps = nfull / uint32_t(T);
   const uint32_t ngroups = full_steps / G;
 
-  pipelined_groups<DT, G, VLOAD>(src, ngroups, [&](const u32x4* buf, uint32_t) {
+  pipelined_groups<DT, G, VLOAD, POL>(src, ngroups, [&](const u32x4* buf, uint32_t) {
     accumulate_group<DT, G>(a, buf);
   });
   for (uint32_t k = ngroups * G; k < full_steps; ++k) {
     float z[VEC];
-    Elt<DT>::decode(fetch<VLOAD>(src, k), z);
+    Elt<DT>::decode(fetch<VLOAD, POL>(src, k), z);
     accumulate<VEC, 1>(a, z);
   }
   if (full_steps * uint32_t(T) < nvec) {
     const uint32_t v = full_steps * uint32_t(T) + tid;
     float z[VEC];
     if (v < nfull) {
-      Elt<DT>::decode(fetch<VLOAD>(src, full_steps), z);
+      Elt<DT>::decode(fetch<VLOAD, POL>(src, full_steps), z);
     } else {
 #pragma unroll
       for (int k = 0; k < VEC; ++k) {
@@ -610,7 +613,7 @@ __device__ inline void bwd_vec(const RowDst<GT, Elt<DT>::VEC>& dst, uint32_t k, 
   dst.template store<VSTORE>(k, g);
 }
 
-template <int DT, int GT, bool VLOAD, bool VSTORE>
+template <int DT, int GT, bool VLOAD, bool VSTORE, int POL = kNonTemporal, bool REV = false>
 __device__ inline void bwd_row(const BwdArgs& p, const RowSrc& src,
                                const RowDst<GT, Elt<DT>::VEC>& dst, int64_t y, int kind,
                                float lse, float w, int T, int tid) {
@@ -637,27 +640,38 @@ __device__ inline void bwd_row(const BwdArgs& p, const RowSrc& src,
     return;
   }
   const uint32_t ngroups = full_steps / G;
-  pipelined_groups<DT, G, VLOAD>(src, ngroups, [&](const u32x4* buf, uint32_t g) {
+  auto groups = [&] {
+    pipelined_groups<DT, G, VLOAD, POL, REV>(src, ngroups, [&](const u32x4* buf, uint32_t g) {
 #pragma unroll
-    for (int i = 0; i < G; ++i) {
-      const uint32_t k = g * G + i;
-      bwd_vec<DT, GT, VLOAD, VSTORE>(dst, k, buf[i], lse, w, yv - k * uint32_t(T), slot, tid);
-    }
-  });
-  for (uint32_t k = ngroups * G; k < full_steps; ++k)
-    bwd_vec<DT, GT, VLOAD, VSTORE>(dst, k, fetch<VLOAD>(src, k), lse, w, yv - k * uint32_t(T),
-                                   slot, tid);
-  if (full_steps * uint32_t(T) < nvec) {
-    const uint32_t k = full_steps, v = k * uint32_t(T) + tid;
-    if (v < nfull) {
-      bwd_vec<DT, GT, VLOAD, VSTORE>(dst, k, fetch<VLOAD>(src, k), lse, w, yv - k * uint32_t(T),
-                                     slot, tid);
-    } else if (v == nfull) {
-      for (int64_t j = int64_t(v) * VEC; j < width; ++j) {
-        const float z = Elt<DT>::load1(src.row, j);
-        dst.store1(j, j == y ? w * (prob(z, lse) - 1.0f) : w * prob(z, lse));
+      for (int i = 0; i < G; ++i) {
+        const uint32_t k = g * G + i;
+        bwd_vec<DT, GT, VLOAD, VSTORE>(dst, k, buf[i], lse, w, yv - k * uint32_t(T), slot, tid);
+      }
+    });
+  };
+  auto rest = [&] {
+    for (uint32_t k = ngroups * G; k < full_steps; ++k)
+      bwd_vec<DT, GT, VLOAD, VSTORE>(dst, k, fetch<VLOAD, POL>(src, k), lse, w,
+                                     yv - k * uint32_t(T), slot, tid);
+    if (full_steps * uint32_t(T) < nvec) {
+      const uint32_t k = full_steps, v = k * uint32_t(T) + tid;
+      if (v < nfull) {
+        bwd_vec<DT, GT, VLOAD, VSTORE>(dst, k, fetch<VLOAD, POL>(src, k), lse, w,
+                                       yv - k * uint32_t(T), slot, tid);
+      } else if (v == nfull) {
+        for (int64_t j = int64_t(v) * VEC; j < width; ++j) {
+          const float z = Elt<DT>::load1(src.row, j);
+          dst.store1(j, j == y ? w * (prob(z, lse) - 1.0f) : w * prob(z, lse));
+        }
       }
     }
+  };
+  if constexpr (REV) {
+    rest();
+    groups();
+  } else {
+    groups();
+    rest();
   }
 }
 
@@ -687,6 +701,105 @@ void bwd_kernel(BwdArgs p) {
     } else {
       bwd_row<DT, GT, false, false>(p, src, dst, y, kind, lse, w, T, tid);
     }
+  }
+}
+
+// ------------------------------------------- fused forward + backward
+//
+// One pass over each row when the per-token weight is known up front: the
+// forward statistics and the gradient come from a single read of the logits
+// (4 bytes per element at bf16/bf16 instead of 6 for the two calls).  The
+// forward accumulates in exactly the order of row_scan and the gradient uses
+// exactly bwd_vec's arithmetic, so every output is bit-identical to
+// bi_logprob_fwd followed by bi_logprob_bwd.
+//
+// The second pass reads the row again; issued right after the first, it is
+// served mostly by the caches, so HBM sees close to one read per element.
+// (Keeping the whole row in registers instead needs ~76 VGPRs of a 128-VGPR
+// budget at V = 151,936 bf16 and spilled.)
+
+struct FusedArgs {
+  const char* logits;
+  char* grad;
+  int64_t n_rows, vocab, row_bytes, grad_row_bytes;
+  const int64_t* labels;
+  int64_t ignore_index;
+  const float* weights;
+  float* logprob;
+  float* entropy;
+  float* lse;
+  int32_t* status_flag;
+};
+
+// The first pass loads with the default cache policy so that the row stays in
+// L2 / the Infinity Cache; the second pass re-reads it non-temporally, newest
+// data first (its groups in reverse order).  Measured on the large bf16
+// workload: 4.1 ms against 5.4-5.6 ms for the two separate calls.
+#ifndef BI_FUSED_P1_POLICY
+#define BI_FUSED_P1_POLICY 0
+#endif
+#ifndef BI_FUSED_P2_POLICY
+#define BI_FUSED_P2_POLICY 2
+#endif
+#ifndef BI_FUSED_REVERSE
+#define BI_FUSED_REVERSE 1
+#endif
+
+// The forward half of a fused row; returns the lse every lane needs.
+__device__ inline float fused_finish_forward(const FusedArgs& p, int64_t row, const Acc& a,
+                                             float* lds, int T, int tid, float zy, bool ignored,
+                                             bool bad) {
+  const Acc r = block_reduce(a, lds, T, tid);
+  if (tid == 0) {
+    const float lse = lse_of(r);
+    if (p.lse) p.lse[row] = lse;
+    if (p.entropy) p.entropy[row] = entropy_of(r);
+    if (p.logprob) p.logprob[row] = bad ? NAN : (ignored ? 0.0f : zy - lse);
+    if (bad && p.status_flag) atomicOr(p.status_flag, BI_FLAG_BAD_LABEL);
+    lds[3 * kMaxWaves] = lse;
+  }
+  __syncthreads();
+  return lds[3 * kMaxWaves];
+}
+
+template <int DT, int GT, bool ALIGNED>
+__global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(8)))
+void fused_reread_kernel(FusedArgs p) {
+  constexpr int VEC = Elt<DT>::VEC;
+  __shared__ float lds[3 * kMaxWaves + 1];
+  const int T = blockDim.x, tid = threadIdx.x;
+  const int64_t width = p.vocab;
+  for (int64_t row = blockIdx.x; row < p.n_rows; row += gridDim.x) {
+    const char* rp = p.logits + row * p.row_bytes;
+    char* gp = p.grad + row * p.grad_row_bytes;
+    const int64_t y = p.labels[row];
+    const bool ignored = y == p.ignore_index;
+    const bool bad = !ignored && (y < 0 || y >= width);
+    float zy = 0.0f;
+    if (tid == 0 && !ignored && !bad) zy = Elt<DT>::load1(rp, y);
+    const float w = (!ignored && !bad && p.weights) ? p.weights[row] : 1.0f;
+    const RowSrc src = row_src(rp, width * (DT == BI_BF16 ? 2 : 4), T, tid);
+    const bool vload = ALIGNED || (reinterpret_cast<uintptr_t>(rp) & 3u) == 0;
+    const bool vstore = ALIGNED || (reinterpret_cast<uintptr_t>(gp) & 3u) == 0;
+    constexpr int P1 = BI_FUSED_P1_POLICY, P2 = BI_FUSED_P2_POLICY;
+    constexpr bool REV = BI_FUSED_REVERSE;
+    Acc a = acc_empty();
+    if (vload) row_scan<DT, true, P1>(a, src, width, T, tid);
+    else row_scan<DT, false, P1>(a, src, width, T, tid);
+    const float lse = fused_finish_forward(p, row, a, lds, T, tid, zy, ignored, bad);
+    const int kind = ignored ? 1 : (bad ? 2 : 0);
+    const RowDst<GT, VEC> dst(gp, T, tid);
+    BwdArgs b{p.logits, p.grad, p.n_rows, width, p.row_bytes, p.grad_row_bytes, p.labels,
+              p.ignore_index, nullptr, nullptr, nullptr};
+    if (ALIGNED || (vload && vstore))
+      bwd_row<DT, GT, true, true, P2, REV>(b, src, dst, y, kind, lse, w, T, tid);
+    else if (vload)
+      bwd_row<DT, GT, true, false, P2, REV>(b, src, dst, y, kind, lse, w, T, tid);
+    else if (vstore)
+      bwd_row<DT, GT, false, true, P2, REV>(b, src, dst, y, kind, lse, w, T, tid);
+    else
+      bwd_row<DT, GT, false, false, P2, REV>(b, src, dst, y, kind, lse, w, T, tid);
+    if (row + gridDim.x < p.n_rows) __syncthreads();
   }
 }
 
@@ -897,6 +1010,52 @@ int bi_logprob_bwd(const void* logits, int dtype, int64_t n_rows, int64_t vocab,
   if (dtype == BI_BF16 && grad_dtype == BI_BF16) launch_bwd<BI_BF16, BI_BF16>(a, g.threads, s);
   else if (dtype == BI_BF16) launch_bwd<BI_BF16, BI_F32>(a, g.threads, s);
   else launch_bwd<BI_F32, BI_F32>(a, g.threads, s);
+  return launched(fn);
+}
+
+int bi_logprob_fwd_bwd(const void* logits, int dtype, int64_t n_rows, int64_t vocab,
+                       int64_t row_stride, const int64_t* labels, int64_t ignore_index,
+                       const float* weights, float* logprob, float* entropy, float* lse,
+                       void* grad, int grad_dtype, int64_t grad_row_stride,
+                       int32_t* status_flag, bi_stream_t stream) {
+  const char* fn = "bi_logprob_fwd_bwd";
+  if (int r = check_dtype(dtype, fn)) return r;
+  if (int r = check_dtype(grad_dtype, fn)) return r;
+  if (dtype == BI_F32 && grad_dtype == BI_BF16)
+    return fail(BI_ERR_DTYPE, "%s: fp32 logits with a bf16 gradient are not supported", fn);
+  if (n_rows < 0) return fail(BI_ERR_SHAPE, "%s: n_rows %lld < 0", fn, (long long)n_rows);
+  if (vocab < 1 || vocab >= kMaxWidth)
+    return fail(BI_ERR_SHAPE, "%s: vocab %lld outside [1, 2^29)", fn, (long long)vocab);
+  if (row_stride < vocab || grad_row_stride < vocab)
+    return fail(BI_ERR_SHAPE, "%s: row strides (%lld, %lld) must be >= vocab %lld", fn,
+                (long long)row_stride, (long long)grad_row_stride, (long long)vocab);
+  if (n_rows == 0) return ok();
+  if (!logits || !labels || !grad)
+    return fail(BI_ERR_NULL, "%s: logits, labels and grad are required", fn);
+  if (!aligned(logits, elem_size(dtype)) || !aligned(grad, elem_size(grad_dtype)) ||
+      !aligned(labels, 8) || !aligned(weights, 4) || !aligned(logprob, 4) ||
+      !aligned(entropy, 4) || !aligned(lse, 4) || !aligned(status_flag, 4))
+    return fail(BI_ERR_ALIGN, "%s: misaligned pointer", fn);
+  FusedArgs a{static_cast<const char*>(logits), static_cast<char*>(grad), n_rows, vocab,
+              row_stride * int64_t(elem_size(dtype)),
+              grad_row_stride * int64_t(elem_size(grad_dtype)), labels, ignore_index, weights,
+              logprob, entropy, lse, status_flag};
+  const Geometry g = row_geometry(dtype, vocab);
+  const bool all_aligned = rows_dword_aligned(logits, a.row_bytes) &&
+                           rows_dword_aligned(grad, a.grad_row_bytes);
+  const dim3 grid(grid_for(n_rows)), block(g.threads);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+#define BI_FUSED_LAUNCH(DT, GT)                                                              \
+  do {                                                                                       \
+    if (all_aligned)                                                                         \
+      hipLaunchKernelGGL((fused_reread_kernel<DT, GT, true>), grid, block, 0, s, a);         \
+    else                                                                                     \
+      hipLaunchKernelGGL((fused_reread_kernel<DT, GT, false>), grid, block, 0, s, a);        \
+  } while (0)
+  if (dtype == BI_BF16 && grad_dtype == BI_BF16) BI_FUSED_LAUNCH(BI_BF16, BI_BF16);
+  else if (dtype == BI_BF16) BI_FUSED_LAUNCH(BI_BF16, BI_F32);
+  else BI_FUSED_LAUNCH(BI_F32, BI_F32);
+#undef BI_FUSED_LAUNCH
   return launched(fn);
 }
 

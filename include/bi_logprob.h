@@ -144,6 +144,23 @@ BI_API int bi_logprob_bwd(const void* logits, int dtype, int64_t n_rows, int64_t
                    void* grad, int grad_dtype, int64_t grad_row_stride,
                    int32_t* status_flag, bi_stream_t stream);
 
+/* Forward and backward in one pass over each row, for callers that know the
+ * per-token weight before the forward: logprob, entropy, lse and the gradient
+ * w * (softmax - onehot), reading the logits once.  Every output is bit-
+ * identical to bi_logprob_fwd followed by bi_logprob_bwd with the same
+ * weights (same lane map, reduction tree and per-element arithmetic).
+ * Defined as the composition of the two calls above (PR #4685, Summary and
+ * Why; Correctness and compatibility for the weights).
+ *   weights      [n_rows] fp32, NULL means 1 (as in bi_logprob_bwd)
+ *   logprob, entropy, lse  [n_rows] fp32 each; each may be NULL
+ *   grad         required; layout and dtype rules as in bi_logprob_bwd
+ */
+BI_API int bi_logprob_fwd_bwd(const void* logits, int dtype, int64_t n_rows, int64_t vocab,
+                              int64_t row_stride, const int64_t* labels, int64_t ignore_index,
+                              const float* weights, float* logprob, float* entropy, float* lse,
+                              void* grad, int grad_dtype, int64_t grad_row_stride,
+                              int32_t* status_flag, bi_stream_t stream);
+
 /* Statistics of one vocabulary chunk: global columns
  * [vocab_offset, vocab_offset + chunk_width) held as a [n_rows, chunk_width]
  * view.  Defined in PR #4685, Why (shard-local sufficient statistics) and the

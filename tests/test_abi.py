@@ -34,7 +34,8 @@ def declared_functions():
 
 def test_header_declares_the_four_entry_points():
     names = declared_functions()
-    for fn in ("bi_logprob_fwd", "bi_logprob_bwd", "bi_vocab_chunk_stats", "bi_stats_combine"):
+    for fn in ("bi_logprob_fwd", "bi_logprob_bwd", "bi_vocab_chunk_stats", "bi_stats_combine",
+               "bi_logprob_fwd_bwd"):
         assert fn in names
 
 
@@ -90,6 +91,24 @@ def test_bwd_argument_errors(L):
     assert bwd(L, grad=P2, gdt=bi.BI_F32) == bi.BI_ERR_ALIGN
     assert bwd(L, w=ctypes.c_void_p(0x10002)) == bi.BI_ERR_ALIGN
     assert bwd(L, n=0, logits=NUL, labels=NUL, lse=NUL, grad=NUL) == bi.BI_OK
+
+
+def fused(L, logits=P, dtype=bi.BI_BF16, n=4, v=100, rs=100, labels=P, w=NUL, lp=NUL,
+          grad=P, gdt=bi.BI_BF16, grs=100, flag=NUL):
+    return L.bi_logprob_fwd_bwd(logits, dtype, n, v, rs, labels, -100, w, lp, NUL, NUL, grad, gdt,
+                                grs, flag, NUL)
+
+
+def test_fused_argument_errors(L):
+    assert fused(L, dtype=bi.BI_F32, gdt=bi.BI_BF16) == bi.BI_ERR_DTYPE
+    assert fused(L, dtype=3) == bi.BI_ERR_DTYPE
+    assert fused(L, grs=99) == bi.BI_ERR_SHAPE
+    assert fused(L, v=0) == bi.BI_ERR_SHAPE
+    assert fused(L, grad=NUL) == bi.BI_ERR_NULL
+    assert fused(L, labels=NUL) == bi.BI_ERR_NULL
+    assert fused(L, w=ctypes.c_void_p(0x10002)) == bi.BI_ERR_ALIGN
+    assert fused(L, lp=ctypes.c_void_p(0x10001)) == bi.BI_ERR_ALIGN
+    assert fused(L, n=0, logits=NUL, labels=NUL, grad=NUL) == bi.BI_OK
 
 
 def chunk(L, logits=P, dtype=bi.BI_BF16, n=4, w=25, rs=100, off=25, v=100, labels=P,

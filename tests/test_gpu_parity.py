@@ -226,3 +226,72 @@ def test_bwd_writes_every_element_deterministically(V, dt, gdt):
     assert not bool(torch.isnan(g1).any())
     ity = torch.int16 if gdt == torch.bfloat16 else torch.int32
     assert torch.equal(g1.view(ity), g2.view(ity))
+
+
+def _fused_vs_two_calls(logits, labels, w, gdt):
+    lp, ent, lse = bi.fwd(logits, labels)
+    g = bi.bwd(logits, labels, lse, w, gdt)
+    flp, fent, flse, fg = bi.fwd_bwd(logits, labels, w, gdt)
+    torch.cuda.synchronize()
+    for a, c in ((lp, flp), (ent, fent), (lse, flse)):
+        assert torch.equal(a.view(torch.int32), c.view(torch.int32))
+    ity = torch.int16 if gdt == torch.bfloat16 else torch.int32
+    assert torch.equal(g.view(ity), fg.view(ity))
+    return flp, fent, flse, fg
+
+
+@pytest.mark.parametrize("V", [1, 7, 16, 65, 1000, 4097, 16_389, 65_539, 151_936, 151_937])
+@pytest.mark.parametrize("dt,gdt", [("bf16", torch.bfloat16), ("bf16", torch.float32),
+                                    ("f32", torch.float32)])
+def test_fused_equals_fwd_then_bwd_bitwise(V, dt, gdt):
+    b = random_batch(7, V, dt, seed=V + 3, ignore_frac=0.2, mask_frac=0.1 if V > 4 else 0.0)
+    logits, labels, w = dev_logits(b.logits, dt), dev(b.labels), dev(b.weights)
+    flp, fent, flse, fg = _fused_vs_two_calls(logits, labels, w, gdt)
+    # and against the oracle
+    grads = {"f32": host(fg)} if gdt == torch.float32 else {}
+    check_against_oracle(b, (host(flp), host(fent), host(flse)), grads)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("pad,offset", [(1, 0), (3, 1)])
+def test_fused_on_strided_unaligned_rows(dt, pad, offset):
+    V, n = 20_011, 6
+    b = random_batch(n, V, dt, seed=21 + pad, ignore_frac=0.2, mask_frac=0.05)
+    stride = V + pad
+    store = np.zeros(offset + n * stride, dtype=b.logits.dtype)
+    for i in range(n):
+        store[offset + i * stride: offset + i * stride + V] = b.logits[i]
+    base = dev_logits(store, dt)
+    view = base[offset:offset + (n - 1) * stride + V].as_strided((n, V), (stride, 1))
+    labels, w = dev(b.labels), dev(b.weights)
+    gdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    gstore = torch.zeros(offset + n * stride, dtype=gdt, device="cuda")
+    gview = gstore[offset:offset + (n - 1) * stride + V].as_strided((n, V), (stride, 1))
+    flp, fent, flse, _ = bi.fwd_bwd(view, labels, w, grad=gview)
+    lp, ent, lse = bi.fwd(dev_logits(b.logits, dt), labels)
+    g = bi.bwd(dev_logits(b.logits, dt), labels, lse, w, gdt)
+    torch.cuda.synchronize()
+    for a, c in ((lp, flp), (ent, fent), (lse, flse)):
+        assert torch.equal(a.view(torch.int32), c.view(torch.int32))
+    ity = torch.int16 if gdt == torch.bfloat16 else torch.int32
+    assert torch.equal(g.view(ity), gview.contiguous().view(ity))
+
+
+def test_fused_bad_labels_and_null_outputs():
+    V = 3000
+    b = random_batch(4, V, "bf16", seed=8)
+    logits = dev_logits(b.logits, "bf16")
+    labels = dev(np.array([5, V + 2, -100, 17]))
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    grad = torch.full((4, V), float("nan"), dtype=torch.float32, device="cuda")
+    lib = bi.lib()
+    import ctypes
+    rc = lib.bi_logprob_fwd_bwd(ctypes.c_void_p(logits.data_ptr()), bi.BI_BF16, 4, V, V,
+                                ctypes.c_void_p(labels.data_ptr()), -100, None, None, None, None,
+                                ctypes.c_void_p(grad.data_ptr()), bi.BI_F32, V,
+                                ctypes.c_void_p(flag.data_ptr()), None)
+    torch.cuda.synchronize()
+    assert rc == 0 and int(flag.item()) == bi.BI_FLAG_BAD_LABEL
+    g = host(grad)
+    assert np.isfinite(g[0]).all() and np.isnan(g[1]).all() and np.all(g[2] == 0)
+    assert np.isfinite(g[3]).all()

@@ -99,20 +99,24 @@ def test_masked_2048_f32_odd_width():
 
 # ------------------------------------------------------------ batch invariance
 
-def _run_rows(batch):
+def _run_rows(batch, fused=False):
     logits, labels, w = dev_logits(batch.logits, "bf16"), dev(batch.labels), dev(batch.weights)
-    lp, ent, lse = bi.fwd(logits, labels)
-    g = bi.bwd(logits, labels, lse, w, torch.bfloat16)
+    if fused:
+        lp, ent, lse, g = bi.fwd_bwd(logits, labels, w, torch.bfloat16)
+    else:
+        lp, ent, lse = bi.fwd(logits, labels)
+        g = bi.bwd(logits, labels, lse, w, torch.bfloat16)
     gf = bi.bwd(logits, labels, lse, w, torch.float32)
     return logits, labels, w, lp, ent, lse, g, gf
 
 
-def test_batch_invariance_sweep():
+@pytest.mark.parametrize("fused", [False, True], ids=["two_calls", "fused"])
+def test_batch_invariance_sweep(fused):
     per_n = {}
     for n, cases in wl.invariance_batches():
         outs = []
         for case in cases:
-            _, _, _, lp, ent, lse, g, gf = _run_rows(case.batch)
+            _, _, _, lp, ent, lse, g, gf = _run_rows(case.batch, fused)
             pos = torch.from_numpy(case.positions).cuda()
             outs.append((lp[pos], ent[pos], lse[pos], g[pos], gf[pos]))
         torch.cuda.synchronize()
@@ -192,6 +196,18 @@ def test_large_fwd_bwd_sampled_rows(large):
     assert_close(host(lse)[rows], olse, tl, "lse")
     check_grads(b, rows, None, host(g32), host(g16[ridx]))
     assert np.all(np.isfinite(host(lp))) and np.all(np.isfinite(host(ent)))
+
+
+def test_large_fused_equals_two_calls(large):
+    logits, labels, w = large["logits"], large["labels"], large["w"]
+    lp, ent, lse = bi.fwd(logits, labels)
+    g = bi.bwd(logits, labels, lse, w, torch.bfloat16)
+    flp, fent, flse, fg = bi.fwd_bwd(logits, labels, w, torch.bfloat16)
+    torch.cuda.synchronize()
+    for a, c in ((lp, flp), (ent, fent), (lse, flse)):
+        assert torch.equal(a.view(torch.int32), c.view(torch.int32))
+    assert torch.equal(g.view(torch.int16), fg.view(torch.int16))
+    del g, fg
 
 
 def test_large_chunked_path_equals_full_rows(large):
