@@ -148,6 +148,23 @@ def main():
                    stream=stream)
         if ev: ev[1].record(stream)
 
+    g = np.random.default_rng([seed, 17])
+    old_lp = torch.from_numpy(g.normal(-11.0, 1.5, N).astype(np.float32)).to(dev)
+    adv = torch.from_numpy(g.standard_normal(N).astype(np.float32)).to(dev)
+    scale = torch.full((N,), 1.0 / N, dtype=torch.float32, device=dev)
+    ploss, pw = torch.empty_like(lp), torch.empty_like(lp)
+
+    def step_policy(ev=None):
+        if ev: ev[0].record(stream)
+        L = bi.lib()
+        rc = L.bi_policy_loss_fwd_bwd(
+            logits.data_ptr(), bi.BI_BF16, N, V, V, labels.data_ptr(), -100, old_lp.data_ptr(),
+            adv.data_ptr(), scale.data_ptr(), 0.2, 0.28, lp.data_ptr(), ent.data_ptr(),
+            lse.data_ptr(), ploss.data_ptr(), pw.data_ptr(), grad.data_ptr(), bi.BI_BF16, V,
+            flag.data_ptr(), stream.cuda_stream)
+        assert rc == 0, rc
+        if ev: ev[1].record(stream)
+
     def step_two_calls(ev=None):
         if ev: ev[0].record(stream)
         bi.fwd(logits, labels, out=(lp, ent, lse), status=flag, stream=stream)
@@ -180,6 +197,7 @@ def main():
         step_fused()
         step_two_calls()
         step_chunked()
+        step_policy()
     torch.cuda.synchronize()
 
     def timed(step, n_events):
@@ -199,6 +217,7 @@ def main():
     # the same work as two calls, and the vocabulary-chunked variant, same run
     ms_two, (t_fwd, t_bwd) = timed(step_two_calls, 3)
     ms_chunked, (t_chunk, t_comb, t_cbwd) = timed(step_chunked, 4)
+    ms_policy, (t_policy,) = timed(step_policy, 2)
     assert int(flag.item()) == 0
 
     f_b, b_b, c_b, m_b = algorithmic_bytes(V, 2, 2, len(bounds))
@@ -225,6 +244,10 @@ def main():
     two_call = {"ms_per_step": ms_two, "rows_per_s": N / (ms_two * 1e-3),
                 "hbm_GBps": gbps(N * (f_b + b_b), ms_two),
                 "pct_hbm_peak": 100 * gbps(N * (f_b + b_b), ms_two) / HBM_PEAK_GBPS}
+    policy = {"ms_per_step": ms_policy, "rows_per_s": N / (ms_policy * 1e-3),
+              "kernel_ms": mean(t_policy), "clip": [0.2, 0.28],
+              "what": "bi_policy_loss_fwd_bwd: logprob, entropy, clipped-ratio loss and its "
+                      "gradient in one pass (weights derived in the kernel)"}
     chunked = {"ms_per_step": ms_chunked, "rows_per_s": N / (ms_chunked * 1e-3),
                "hbm_GBps": gbps(N * (c_b + m_b + b_b), ms_chunked),
                "bwd_ms": mean(t_cbwd)}
@@ -255,6 +278,7 @@ def main():
         "kernels": kernels,
         "two_call": two_call,
         "chunked": chunked,
+        "policy_loss": policy,
         "input_gen_s": gen_s,
     }
     if not args.no_cpu_baseline and not args.profile_steps:

@@ -21,7 +21,7 @@ from typing import Optional, Tuple
 import torch  # first: the library then binds to the HIP runtime torch has loaded
 
 __all__ = [
-    "IGNORE_INDEX", "BiError", "fwd", "bwd", "fwd_bwd", "vocab_chunk_stats", "stats_combine",
+    "IGNORE_INDEX", "BiError", "fwd", "bwd", "fwd_bwd", "policy_loss_fwd_bwd", "vocab_chunk_stats", "stats_combine",
     "row_geometry", "LogprobEntropy", "logprob_entropy", "lib", "library_path",
 ]
 
@@ -79,11 +79,15 @@ def lib() -> ctypes.CDLL:
     L.bi_logprob_bwd.argtypes = [vp, i32, i64, i64, i64, vp, i64, vp, vp, vp, i32, i64, vp, vp]
     L.bi_logprob_fwd_bwd.argtypes = [vp, i32, i64, i64, i64, vp, i64, vp, vp, vp, vp, vp, i32,
                                      i64, vp, vp]
+    f32 = ctypes.c_float
+    L.bi_policy_loss_fwd_bwd.argtypes = [vp, i32, i64, i64, i64, vp, i64, vp, vp, vp, f32, f32,
+                                         vp, vp, vp, vp, vp, vp, i32, i64, vp, vp]
     L.bi_vocab_chunk_stats.argtypes = [vp, i32, i64, i64, i64, i64, i64, vp, i64, vp, vp, vp]
     L.bi_stats_combine.argtypes = [vp, i64, i64, vp, i64, vp, vp, vp, vp]
     L.bi_row_geometry.argtypes = [i32, i64, ctypes.POINTER(i32), ctypes.POINTER(i32),
                                   ctypes.POINTER(i32)]
-    for fn in ("bi_logprob_fwd", "bi_logprob_bwd", "bi_logprob_fwd_bwd", "bi_vocab_chunk_stats",
+    for fn in ("bi_logprob_fwd", "bi_logprob_bwd", "bi_logprob_fwd_bwd",
+               "bi_policy_loss_fwd_bwd", "bi_vocab_chunk_stats",
                "bi_stats_combine", "bi_row_geometry"):
         getattr(L, fn).restype = i32
     L.bi_status_string.argtypes = [i32]
@@ -211,6 +215,38 @@ def fwd_bwd(logits: torch.Tensor, labels: torch.Tensor, weights: Optional[torch.
         _ptr(weights), _ptr(lp), _ptr(ent), _ptr(lse), _ptr(grad), _dtype_code(grad.dtype), grs,
         _ptr(status), _stream(stream)))
     return lp, ent, lse, grad
+
+
+def policy_loss_fwd_bwd(logits: torch.Tensor, labels: torch.Tensor, old_logprob: torch.Tensor,
+                        advantages: torch.Tensor, clip_low: float = 0.2, clip_high: float = 0.28,
+                        loss_scale: Optional[torch.Tensor] = None,
+                        grad_dtype: Optional[torch.dtype] = None,
+                        ignore_index: int = IGNORE_INDEX, *, grad: Optional[torch.Tensor] = None,
+                        status: Optional[torch.Tensor] = None, stream=None):
+    """Clipped-ratio policy loss in one pass over each row.
+
+    Returns (logprob, entropy, lse, loss, weight, grad): per-token fp32 vectors
+    and the gradient of the loss with respect to the logits.
+    """
+    n, v, rs = _rows(logits, "logits")
+    _vec(labels, n, torch.int64, "labels")
+    _vec(old_logprob, n, torch.float32, "old_logprob")
+    _vec(advantages, n, torch.float32, "advantages")
+    _vec(loss_scale, n, torch.float32, "loss_scale")
+    _vec(status, 1, torch.int32, "status")
+    outs = tuple(torch.empty(n, dtype=torch.float32, device=logits.device) for _ in range(5))
+    if grad is None:
+        grad = torch.empty((n, v), dtype=grad_dtype or logits.dtype, device=logits.device)
+    gn, gv, grs = _rows(grad, "grad")
+    if (gn, gv) != (n, v):
+        raise ValueError("grad must have the logits' shape")
+    lp, ent, lse, loss, w = outs
+    _check("bi_policy_loss_fwd_bwd", lib().bi_policy_loss_fwd_bwd(
+        _ptr(logits), _dtype_code(logits.dtype), n, v, rs, _ptr(labels), ignore_index,
+        _ptr(old_logprob), _ptr(advantages), _ptr(loss_scale), float(clip_low), float(clip_high),
+        _ptr(lp), _ptr(ent), _ptr(lse), _ptr(loss), _ptr(w), _ptr(grad), _dtype_code(grad.dtype),
+        grs, _ptr(status), _stream(stream)))
+    return lp, ent, lse, loss, w, grad
 
 
 def vocab_chunk_stats(logits_chunk: torch.Tensor, labels: torch.Tensor, vocab_offset: int,

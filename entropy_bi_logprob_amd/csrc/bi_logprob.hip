@@ -729,7 +729,29 @@ struct FusedArgs {
   float* entropy;
   float* lse;
   int32_t* status_flag;
+  // clipped-ratio policy loss (POLICY kernels only)
+  const float* old_logprob;
+  const float* advantages;
+  const float* loss_scale;
+  float clip_low, clip_high;
+  float* loss;
+  float* weight_out;
 };
+
+// Weight of the clipped-ratio surrogate for one token (thread 0 only):
+// r = exp(logprob - old), surrogate min(r A, clip(r, 1 - lo, 1 + hi) A), loss
+// = -c * surrogate, weight = -d loss / d logprob = c A r where the unclipped
+// term is the minimum (ties count as unclipped), else 0.
+__device__ inline float policy_weight(const FusedArgs& p, int64_t row, float logprob,
+                                      float* loss) {
+  const float r = exp2_hw((logprob - p.old_logprob[row]) * kLog2e);
+  const float A = p.advantages[row];
+  const float c = p.loss_scale ? p.loss_scale[row] : 1.0f;
+  const float rc = fminf(fmaxf(r, 1.0f - p.clip_low), 1.0f + p.clip_high);
+  const bool unclipped = r * A <= rc * A;
+  *loss = -c * (unclipped ? r * A : rc * A);
+  return unclipped ? (c * A) * r : 0.0f;
+}
 
 // The first pass loads with the default cache policy so that the row stays in
 // L2 / the Infinity Cache; the second pass re-reads it non-temporally, newest
@@ -745,28 +767,39 @@ struct FusedArgs {
 #define BI_FUSED_REVERSE 1
 #endif
 
-// The forward half of a fused row; returns the lse every lane needs.
-__device__ inline float fused_finish_forward(const FusedArgs& p, int64_t row, const Acc& a,
-                                             float* lds, int T, int tid, float zy, bool ignored,
-                                             bool bad) {
+// The forward half of a fused row.  Every lane gets the lse and the weight of
+// the gradient (the given one, or the policy-loss weight when POLICY).
+template <bool POLICY>
+__device__ inline void fused_finish_forward(const FusedArgs& p, int64_t row, const Acc& a,
+                                            float* lds, int T, int tid, float zy, bool ignored,
+                                            bool bad, float* lse_out, float* w_out) {
   const Acc r = block_reduce(a, lds, T, tid);
   if (tid == 0) {
     const float lse = lse_of(r);
+    const float lp = bad ? NAN : (ignored ? 0.0f : zy - lse);
     if (p.lse) p.lse[row] = lse;
     if (p.entropy) p.entropy[row] = entropy_of(r);
-    if (p.logprob) p.logprob[row] = bad ? NAN : (ignored ? 0.0f : zy - lse);
+    if (p.logprob) p.logprob[row] = lp;
     if (bad && p.status_flag) atomicOr(p.status_flag, BI_FLAG_BAD_LABEL);
     lds[3 * kMaxWaves] = lse;
+    if constexpr (POLICY) {
+      float loss = bad ? NAN : 0.0f, w = bad ? NAN : 0.0f;
+      if (!ignored && !bad) w = policy_weight(p, row, lp, &loss);
+      if (p.loss) p.loss[row] = loss;
+      if (p.weight_out) p.weight_out[row] = w;
+      lds[3 * kMaxWaves + 1] = w;
+    }
   }
   __syncthreads();
-  return lds[3 * kMaxWaves];
+  *lse_out = lds[3 * kMaxWaves];
+  if constexpr (POLICY) *w_out = lds[3 * kMaxWaves + 1];
 }
 
-template <int DT, int GT, bool ALIGNED>
+template <int DT, int GT, bool ALIGNED, bool POLICY>
 __global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(8)))
 void fused_reread_kernel(FusedArgs p) {
   constexpr int VEC = Elt<DT>::VEC;
-  __shared__ float lds[3 * kMaxWaves + 1];
+  __shared__ float lds[3 * kMaxWaves + 2];
   const int T = blockDim.x, tid = threadIdx.x;
   const int64_t width = p.vocab;
   for (int64_t row = blockIdx.x; row < p.n_rows; row += gridDim.x) {
@@ -777,7 +810,7 @@ void fused_reread_kernel(FusedArgs p) {
     const bool bad = !ignored && (y < 0 || y >= width);
     float zy = 0.0f;
     if (tid == 0 && !ignored && !bad) zy = Elt<DT>::load1(rp, y);
-    const float w = (!ignored && !bad && p.weights) ? p.weights[row] : 1.0f;
+    float w = (!POLICY && !ignored && !bad && p.weights) ? p.weights[row] : 1.0f;
     const RowSrc src = row_src(rp, width * (DT == BI_BF16 ? 2 : 4), T, tid);
     const bool vload = ALIGNED || (reinterpret_cast<uintptr_t>(rp) & 3u) == 0;
     const bool vstore = ALIGNED || (reinterpret_cast<uintptr_t>(gp) & 3u) == 0;
@@ -786,7 +819,8 @@ void fused_reread_kernel(FusedArgs p) {
     Acc a = acc_empty();
     if (vload) row_scan<DT, true, P1>(a, src, width, T, tid);
     else row_scan<DT, false, P1>(a, src, width, T, tid);
-    const float lse = fused_finish_forward(p, row, a, lds, T, tid, zy, ignored, bad);
+    float lse;
+    fused_finish_forward<POLICY>(p, row, a, lds, T, tid, zy, ignored, bad, &lse, &w);
     const int kind = ignored ? 1 : (bad ? 2 : 0);
     const RowDst<GT, VEC> dst(gp, T, tid);
     BwdArgs b{p.logits, p.grad, p.n_rows, width, p.row_bytes, p.grad_row_bytes, p.labels,
@@ -892,6 +926,47 @@ void launch_bwd(const BwdArgs& a, int threads, hipStream_t s) {
     hipLaunchKernelGGL((bwd_kernel<DT, GT, true>), grid, block, 0, s, a);
   else
     hipLaunchKernelGGL((bwd_kernel<DT, GT, false>), grid, block, 0, s, a);
+}
+
+template <bool POLICY>
+int launch_fused(const char* fn, FusedArgs a, int dtype, int grad_dtype, int64_t row_stride,
+                 int64_t grad_row_stride, bi_stream_t stream) {
+  if (int r = check_dtype(dtype, fn)) return r;
+  if (int r = check_dtype(grad_dtype, fn)) return r;
+  if (dtype == BI_F32 && grad_dtype == BI_BF16)
+    return fail(BI_ERR_DTYPE, "%s: fp32 logits with a bf16 gradient are not supported", fn);
+  if (a.n_rows < 0) return fail(BI_ERR_SHAPE, "%s: n_rows %lld < 0", fn, (long long)a.n_rows);
+  if (a.vocab < 1 || a.vocab >= kMaxWidth)
+    return fail(BI_ERR_SHAPE, "%s: vocab %lld outside [1, 2^29)", fn, (long long)a.vocab);
+  if (row_stride < a.vocab || grad_row_stride < a.vocab)
+    return fail(BI_ERR_SHAPE, "%s: row strides (%lld, %lld) must be >= vocab %lld", fn,
+                (long long)row_stride, (long long)grad_row_stride, (long long)a.vocab);
+  if (a.n_rows == 0) return ok();
+  if (!a.logits || !a.labels || !a.grad)
+    return fail(BI_ERR_NULL, "%s: logits, labels and grad are required", fn);
+  if (!aligned(a.logits, elem_size(dtype)) || !aligned(a.grad, elem_size(grad_dtype)) ||
+      !aligned(a.labels, 8) || !aligned(a.weights, 4) || !aligned(a.logprob, 4) ||
+      !aligned(a.entropy, 4) || !aligned(a.lse, 4) || !aligned(a.status_flag, 4))
+    return fail(BI_ERR_ALIGN, "%s: misaligned pointer", fn);
+  a.row_bytes = row_stride * int64_t(elem_size(dtype));
+  a.grad_row_bytes = grad_row_stride * int64_t(elem_size(grad_dtype));
+  const Geometry g = row_geometry(dtype, a.vocab);
+  const bool all_aligned = rows_dword_aligned(a.logits, a.row_bytes) &&
+                           rows_dword_aligned(a.grad, a.grad_row_bytes);
+  const dim3 grid(grid_for(a.n_rows)), block(g.threads);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+#define BI_FUSED_LAUNCH(DT, GT)                                                              \
+  do {                                                                                       \
+    if (all_aligned)                                                                         \
+      hipLaunchKernelGGL((fused_reread_kernel<DT, GT, true, POLICY>), grid, block, 0, s, a); \
+    else                                                                                     \
+      hipLaunchKernelGGL((fused_reread_kernel<DT, GT, false, POLICY>), grid, block, 0, s, a);\
+  } while (0)
+  if (dtype == BI_BF16 && grad_dtype == BI_BF16) BI_FUSED_LAUNCH(BI_BF16, BI_BF16);
+  else if (dtype == BI_BF16) BI_FUSED_LAUNCH(BI_BF16, BI_F32);
+  else BI_FUSED_LAUNCH(BI_F32, BI_F32);
+#undef BI_FUSED_LAUNCH
+  return launched(fn);
 }
 
 }  // namespace
@@ -1018,45 +1093,33 @@ int bi_logprob_fwd_bwd(const void* logits, int dtype, int64_t n_rows, int64_t vo
                        const float* weights, float* logprob, float* entropy, float* lse,
                        void* grad, int grad_dtype, int64_t grad_row_stride,
                        int32_t* status_flag, bi_stream_t stream) {
-  const char* fn = "bi_logprob_fwd_bwd";
-  if (int r = check_dtype(dtype, fn)) return r;
-  if (int r = check_dtype(grad_dtype, fn)) return r;
-  if (dtype == BI_F32 && grad_dtype == BI_BF16)
-    return fail(BI_ERR_DTYPE, "%s: fp32 logits with a bf16 gradient are not supported", fn);
-  if (n_rows < 0) return fail(BI_ERR_SHAPE, "%s: n_rows %lld < 0", fn, (long long)n_rows);
-  if (vocab < 1 || vocab >= kMaxWidth)
-    return fail(BI_ERR_SHAPE, "%s: vocab %lld outside [1, 2^29)", fn, (long long)vocab);
-  if (row_stride < vocab || grad_row_stride < vocab)
-    return fail(BI_ERR_SHAPE, "%s: row strides (%lld, %lld) must be >= vocab %lld", fn,
-                (long long)row_stride, (long long)grad_row_stride, (long long)vocab);
-  if (n_rows == 0) return ok();
-  if (!logits || !labels || !grad)
-    return fail(BI_ERR_NULL, "%s: logits, labels and grad are required", fn);
-  if (!aligned(logits, elem_size(dtype)) || !aligned(grad, elem_size(grad_dtype)) ||
-      !aligned(labels, 8) || !aligned(weights, 4) || !aligned(logprob, 4) ||
-      !aligned(entropy, 4) || !aligned(lse, 4) || !aligned(status_flag, 4))
+  FusedArgs a{static_cast<const char*>(logits), static_cast<char*>(grad), n_rows, vocab,
+              0, 0, labels, ignore_index, weights, logprob, entropy, lse, status_flag,
+              nullptr, nullptr, nullptr, 0.0f, 0.0f, nullptr, nullptr};
+  return launch_fused<false>("bi_logprob_fwd_bwd", a, dtype, grad_dtype, row_stride,
+                             grad_row_stride, stream);
+}
+
+int bi_policy_loss_fwd_bwd(const void* logits, int dtype, int64_t n_rows, int64_t vocab,
+                           int64_t row_stride, const int64_t* labels, int64_t ignore_index,
+                           const float* old_logprob, const float* advantages,
+                           const float* loss_scale, float clip_low, float clip_high,
+                           float* logprob, float* entropy, float* lse, float* loss,
+                           float* weight, void* grad, int grad_dtype, int64_t grad_row_stride,
+                           int32_t* status_flag, bi_stream_t stream) {
+  const char* fn = "bi_policy_loss_fwd_bwd";
+  if (!(clip_low >= 0.0f && clip_low < 1.0f) || !(clip_high >= 0.0f && clip_high < 1e30f))
+    return fail(BI_ERR_SHAPE, "%s: clip bounds must satisfy 0 <= clip_low < 1, 0 <= clip_high",
+                fn);
+  if (n_rows > 0 && (!old_logprob || !advantages))
+    return fail(BI_ERR_NULL, "%s: old_logprob and advantages are required", fn);
+  if (!aligned(old_logprob, 4) || !aligned(advantages, 4) || !aligned(loss_scale, 4) ||
+      !aligned(loss, 4) || !aligned(weight, 4))
     return fail(BI_ERR_ALIGN, "%s: misaligned pointer", fn);
   FusedArgs a{static_cast<const char*>(logits), static_cast<char*>(grad), n_rows, vocab,
-              row_stride * int64_t(elem_size(dtype)),
-              grad_row_stride * int64_t(elem_size(grad_dtype)), labels, ignore_index, weights,
-              logprob, entropy, lse, status_flag};
-  const Geometry g = row_geometry(dtype, vocab);
-  const bool all_aligned = rows_dword_aligned(logits, a.row_bytes) &&
-                           rows_dword_aligned(grad, a.grad_row_bytes);
-  const dim3 grid(grid_for(n_rows)), block(g.threads);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-#define BI_FUSED_LAUNCH(DT, GT)                                                              \
-  do {                                                                                       \
-    if (all_aligned)                                                                         \
-      hipLaunchKernelGGL((fused_reread_kernel<DT, GT, true>), grid, block, 0, s, a);         \
-    else                                                                                     \
-      hipLaunchKernelGGL((fused_reread_kernel<DT, GT, false>), grid, block, 0, s, a);        \
-  } while (0)
-  if (dtype == BI_BF16 && grad_dtype == BI_BF16) BI_FUSED_LAUNCH(BI_BF16, BI_BF16);
-  else if (dtype == BI_BF16) BI_FUSED_LAUNCH(BI_BF16, BI_F32);
-  else BI_FUSED_LAUNCH(BI_F32, BI_F32);
-#undef BI_FUSED_LAUNCH
-  return launched(fn);
+              0, 0, labels, ignore_index, nullptr, logprob, entropy, lse, status_flag,
+              old_logprob, advantages, loss_scale, clip_low, clip_high, loss, weight};
+  return launch_fused<true>(fn, a, dtype, grad_dtype, row_stride, grad_row_stride, stream);
 }
 
 int bi_stats_combine(const bi_stats* stats, int64_t n_chunks, int64_t n_rows,

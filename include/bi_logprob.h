@@ -161,6 +161,34 @@ BI_API int bi_logprob_fwd_bwd(const void* logits, int dtype, int64_t n_rows, int
                               void* grad, int grad_dtype, int64_t grad_row_stride,
                               int32_t* status_flag, bi_stream_t stream);
 
+/* The same single pass, with the per-token weight derived in the kernel from
+ * the logprob it has just computed: the clipped-ratio policy-gradient
+ * surrogate of DAPO/GRPO-style losses ("torchtitan-batch-invarient-GDN",
+ * MATH recipe: DAPO with clip (0.2, 0.28); PR #4685, Summary: per-token
+ * gradients for DAPO/GRPO losses).  Per token, with r = exp(logprob -
+ * old_logprob), advantage A and scale c:
+ *   loss   = -c * min(r A, clip(r, 1 - clip_low, 1 + clip_high) A)
+ *   weight = -d loss / d logprob = c A r if the unclipped term is the minimum
+ *            (ties count as unclipped), else 0
+ *   grad   = weight * (softmax - onehot)  = d loss / d logits
+ * Ignored tokens have loss 0, weight 0 and a zero gradient row.  logprob,
+ * entropy and lse are bit-identical to bi_logprob_fwd, and the gradient to
+ * bi_logprob_bwd given the written weights.
+ *   old_logprob, advantages  [n_rows] fp32, required (the behaviour policy's
+ *                logprob of the label and the token's advantage)
+ *   loss_scale   [n_rows] fp32, NULL means 1 (e.g. 1 / number of tokens)
+ *   clip_low     in [0, 1); clip_high >= 0
+ *   loss, weight [n_rows] fp32 outputs, each may be NULL
+ */
+BI_API int bi_policy_loss_fwd_bwd(const void* logits, int dtype, int64_t n_rows, int64_t vocab,
+                                  int64_t row_stride, const int64_t* labels,
+                                  int64_t ignore_index, const float* old_logprob,
+                                  const float* advantages, const float* loss_scale,
+                                  float clip_low, float clip_high, float* logprob,
+                                  float* entropy, float* lse, float* loss, float* weight,
+                                  void* grad, int grad_dtype, int64_t grad_row_stride,
+                                  int32_t* status_flag, bi_stream_t stream);
+
 /* Statistics of one vocabulary chunk: global columns
  * [vocab_offset, vocab_offset + chunk_width) held as a [n_rows, chunk_width]
  * view.  Defined in PR #4685, Why (shard-local sufficient statistics) and the

@@ -252,6 +252,38 @@ def combine(stats: np.ndarray, labels: np.ndarray, vocab: int,
 
 
 # ---------------------------------------------------------------------------
+# clipped-ratio policy loss per token (the weight of the fused backward)
+# ("torchtitan-batch-invarient-GDN", MATH recipe: DAPO with clip (0.2, 0.28);
+#  "[RL] Avoid full-vocab gather ...", Summary: per-token gradients for
+#  DAPO/GRPO losses)
+# ---------------------------------------------------------------------------
+
+def policy_terms(logprob, old_logprob, advantages, clip_low, clip_high, loss_scale=None,
+                 ignored=None):
+    """Per-token (loss, weight, clipped) of the clipped-ratio surrogate.
+
+    r = exp(logprob - old_logprob); the surrogate is min(r A, clip(r, 1 - lo,
+    1 + hi) A) and the token's loss is -c times it.  The weight is
+    w = -d loss / d logprob = c A r where the unclipped term is the minimum
+    (ties count as unclipped) and 0 where the clipped term is strictly
+    smaller.  Ignored tokens have loss 0 and weight 0.
+    """
+    lp = np.asarray(logprob, dtype=np.float64)
+    r = np.exp(lp - np.asarray(old_logprob, dtype=np.float64))
+    A = np.asarray(advantages, dtype=np.float64)
+    c = np.ones_like(lp) if loss_scale is None else np.asarray(loss_scale, dtype=np.float64)
+    rc = np.minimum(np.maximum(r, 1.0 - clip_low), 1.0 + clip_high)
+    unclipped = r * A <= rc * A
+    loss = -c * np.where(unclipped, r * A, rc * A)
+    w = np.where(unclipped, c * A * r, 0.0)
+    if ignored is not None:
+        ign = np.asarray(ignored, dtype=bool)
+        loss = np.where(ign, 0.0, loss)
+        w = np.where(ign, 0.0, w)
+    return loss, w, ~unclipped
+
+
+# ---------------------------------------------------------------------------
 # brute force: 50-digit textbook softmax, different formula, tiny V only
 # ---------------------------------------------------------------------------
 

@@ -35,7 +35,7 @@ def declared_functions():
 def test_header_declares_the_four_entry_points():
     names = declared_functions()
     for fn in ("bi_logprob_fwd", "bi_logprob_bwd", "bi_vocab_chunk_stats", "bi_stats_combine",
-               "bi_logprob_fwd_bwd"):
+               "bi_logprob_fwd_bwd", "bi_policy_loss_fwd_bwd"):
         assert fn in names
 
 
@@ -109,6 +109,21 @@ def test_fused_argument_errors(L):
     assert fused(L, w=ctypes.c_void_p(0x10002)) == bi.BI_ERR_ALIGN
     assert fused(L, lp=ctypes.c_void_p(0x10001)) == bi.BI_ERR_ALIGN
     assert fused(L, n=0, logits=NUL, labels=NUL, grad=NUL) == bi.BI_OK
+
+
+def policy(L, old=P, adv=P, lo=0.2, hi=0.28, n=4, loss=NUL):
+    return L.bi_policy_loss_fwd_bwd(P, bi.BI_BF16, n, 100, 100, P, -100, old, adv, NUL, lo, hi,
+                                    NUL, NUL, NUL, loss, NUL, P, bi.BI_BF16, 100, NUL, NUL)
+
+
+def test_policy_argument_errors(L):
+    assert policy(L, lo=1.0) == bi.BI_ERR_SHAPE
+    assert policy(L, lo=-0.1) == bi.BI_ERR_SHAPE
+    assert policy(L, hi=float("nan")) == bi.BI_ERR_SHAPE
+    assert policy(L, old=NUL) == bi.BI_ERR_NULL
+    assert policy(L, adv=NUL) == bi.BI_ERR_NULL
+    assert policy(L, loss=ctypes.c_void_p(0x10002)) == bi.BI_ERR_ALIGN
+    assert policy(L, n=0, old=NUL, adv=NUL) == bi.BI_OK
 
 
 def chunk(L, logits=P, dtype=bi.BI_BF16, n=4, w=25, rs=100, off=25, v=100, labels=P,

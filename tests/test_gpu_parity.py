@@ -295,3 +295,41 @@ def test_fused_bad_labels_and_null_outputs():
     g = host(grad)
     assert np.isfinite(g[0]).all() and np.isnan(g[1]).all() and np.all(g[2] == 0)
     assert np.isfinite(g[3]).all()
+
+
+@pytest.mark.parametrize("dt,V", [("bf16", 151_936), ("f32", 65_539), ("bf16", 1000)])
+def test_policy_loss_against_oracle_and_two_calls(dt, V):
+    n, lo, hi = 48, 0.2, 0.28
+    b = random_batch(n, V, dt, seed=V + 11, ignore_frac=0.15, mask_frac=0.05)
+    z = orc.decode(b.logits, dt)
+    olp, _, olse = orc.forward(z, b.labels)
+    g = np.random.default_rng([V, 5])
+    # behaviour logprobs around the current ones, so ratios span both clip sides
+    old = (olp - g.uniform(-0.5, 0.5, n)).astype(np.float32)
+    adv = g.standard_normal(n).astype(np.float32)
+    scale = np.full(n, 1.0 / n, dtype=np.float32)
+    logits, labels = dev_logits(b.logits, dt), dev(b.labels)
+    gdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    lp, ent, lse, loss, w, grad = bi.policy_loss_fwd_bwd(
+        logits, labels, dev(old), dev(adv), lo, hi, dev(scale), gdt)
+    lp2, ent2, lse2 = bi.fwd(logits, labels)
+    g2 = bi.bwd(logits, labels, lse2, w, gdt)
+    torch.cuda.synchronize()
+    for a, c in ((lp, lp2), (ent, ent2), (lse, lse2)):
+        assert torch.equal(a.view(torch.int32), c.view(torch.int32))
+    ity = torch.int16 if gdt == torch.bfloat16 else torch.int32
+    assert torch.equal(grad.view(ity), g2.view(ity))
+    # weights and losses against the fp64 oracle
+    ign = b.labels == -100
+    oloss, ow, ocl = orc.policy_terms(olp, old, adv, lo, hi, scale, ign)
+    w, loss = host(w), host(loss)
+    r = np.exp(olp - old)
+    edge = (np.abs(r - (1 - lo)) < 1e-4) | (np.abs(r - (1 + hi)) < 1e-4)
+    sure = ~edge
+    assert np.abs(w[sure] - ow[sure]).max() <= 1e-5 * max(1.0, np.abs(ow).max())
+    assert np.abs(loss[sure] - oloss[sure]).max() <= 1e-5 * max(1.0, np.abs(oloss).max())
+    # near a clip boundary either branch is correct: zero, or c A r
+    for i in np.nonzero(edge & ~ign)[0]:
+        assert w[i] == 0.0 or abs(w[i] - scale[i] * adv[i] * r[i]) <= 1e-5
+    assert np.all(w[ign] == 0) and np.all(loss[ign] == 0)
+    assert 0 < ocl[~ign].sum() < (~ign).sum()        # both branches are exercised

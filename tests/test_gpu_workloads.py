@@ -210,6 +210,32 @@ def test_large_fused_equals_two_calls(large):
     del g, fg
 
 
+def test_large_policy_loss_matches_two_calls(large):
+    b = large["b"]
+    logits, labels = large["logits"], large["labels"]
+    g = np.random.default_rng([b.rows, 17])
+    old = torch.from_numpy(g.normal(-11.0, 1.5, b.rows).astype(np.float32)).cuda()
+    adv = torch.from_numpy(g.standard_normal(b.rows).astype(np.float32)).cuda()
+    lp, ent, lse, loss, w, grad = bi.policy_loss_fwd_bwd(logits, labels, old, adv, 0.2, 0.28)
+    lp2, ent2, lse2 = bi.fwd(logits, labels)
+    g2 = bi.bwd(logits, labels, lse2, w, torch.bfloat16)
+    torch.cuda.synchronize()
+    for a, c in ((lp, lp2), (ent, ent2), (lse, lse2)):
+        assert torch.equal(a.view(torch.int32), c.view(torch.int32))
+    assert torch.equal(grad.view(torch.int16), g2.view(torch.int16))
+    # sampled rows: weight and loss against the oracle
+    rows = sample_rows(b.rows, 64, seed=9)
+    olp, _, _ = orc.forward(orc.decode(b.logits[rows], "bf16"), b.labels[rows])
+    oldh, advh = host(old)[rows], host(adv)[rows]
+    oloss, ow, _ = orc.policy_terms(olp, oldh, advh, 0.2, 0.28)
+    r = np.exp(olp - oldh)
+    sure = (np.abs(r - 0.8) > 1e-4 * r) & (np.abs(r - 1.28) > 1e-4 * r)
+    wr, lr = host(w)[rows], host(loss)[rows]
+    assert np.all(np.abs(wr - ow)[sure] <= 1e-5 * np.maximum(1.0, np.abs(ow[sure])))
+    assert np.all(np.abs(lr - oloss)[sure] <= 1e-5 * np.maximum(1.0, np.abs(oloss[sure])))
+    del grad, g2
+
+
 def test_large_chunked_path_equals_full_rows(large):
     b = large["b"]
     logits, labels = large["logits"], large["labels"]

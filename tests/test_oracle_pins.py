@@ -361,8 +361,18 @@ def _pin_blocks():
     def bf16():
         return orc.decode(np.array([0x3F80, 0xC040], np.uint16), "bf16").tolist() == [1.0, -3.0]
 
+    def policy():
+        lo, hi = 0.2, 0.28
+        lp = np.log(np.array([0.5, 0.9, 1.5, 0.5, 1.5]))
+        A = np.array([2.0, 1.0, 2.0, -1.0, -1.0])
+        loss, w, cl = orc.policy_terms(lp, np.zeros(5), A, lo, hi)
+        want_w = np.array([1.0, 0.9, 0.0, 0.0, -1.5])
+        want_loss = np.array([-1.0, -0.9, -2.56, 0.8, 1.5])
+        return bool(np.allclose(w, want_w, atol=1e-12) and np.allclose(loss, want_loss, atol=1e-12))
+
     return [("uniform", uniform), ("dominant", dominant), ("brute", brute),
-            ("square_batch", square_batch), ("combine", combine), ("bf16", bf16)]
+            ("square_batch", square_batch), ("combine", combine), ("bf16", bf16),
+            ("policy", policy)]
 
 
 def _core_pin_failures():
@@ -387,7 +397,7 @@ def _mutations():
     o = orc
     real = {n: getattr(o, n) for n in ("weighted_sum", "finalize", "denominator",
                                        "target_logit", "backward", "combine", "decode",
-                                       "row_max", "softmax_from_lse")}
+                                       "row_max", "softmax_from_lse", "policy_terms")}
 
     def drop_u(d, keep):
         return np.zeros(d.shape[0])
@@ -438,7 +448,21 @@ def _mutations():
     def softmax_wrong_ref(z, lse):
         return real["softmax_from_lse"](z, lse - 0.5)
 
+    def policy_clip_swapped(logprob, old_logprob, advantages, clip_low, clip_high,
+                            loss_scale=None, ignored=None):
+        return real["policy_terms"](logprob, old_logprob, advantages, clip_high, clip_low,
+                                    loss_scale, ignored)
+
+    def policy_weight_without_ratio(logprob, old_logprob, advantages, clip_low, clip_high,
+                                    loss_scale=None, ignored=None):
+        loss, w, cl = real["policy_terms"](logprob, old_logprob, advantages, clip_low, clip_high,
+                                           loss_scale, ignored)
+        r = np.exp(np.asarray(logprob, float) - np.asarray(old_logprob, float))
+        return loss, np.where(cl, 0.0, w / r), cl
+
     return {
+        "policy_clip_swapped": ("policy_terms", policy_clip_swapped),
+        "policy_weight_without_ratio": ("policy_terms", policy_weight_without_ratio),
         "drop_weighted_sum": ("weighted_sum", drop_u),
         "entropy_sign": ("finalize", entropy_sign),
         "denominator_shift": ("denominator", no_shift),
@@ -458,3 +482,63 @@ def test_planted_mistakes(name, monkeypatch):
     attr, fn = _mutations()[name]
     monkeypatch.setattr(orc, attr, fn)
     assert _core_pin_failures(), f"planted mistake {name!r} went unnoticed"
+
+
+# ------------------------------------------------- clipped-ratio policy terms
+
+def test_policy_terms_closed_cases():
+    lo, hi = 0.2, 0.28
+    # r = 1 exactly: unclipped, w = c A
+    loss, w, cl = orc.policy_terms([-2.0], [-2.0], [1.5], lo, hi, [0.5])
+    assert w[0] == 0.75 and loss[0] == -0.75 and not cl[0]
+    # A > 0, r above 1 + hi: clipped, no gradient, loss = -c A (1 + hi)
+    lp, old = np.log(1.5), 0.0
+    loss, w, cl = orc.policy_terms([lp], [old], [2.0], lo, hi)
+    assert w[0] == 0.0 and cl[0] and loss[0] == pytest.approx(-2.0 * 1.28)
+    # A > 0, r below 1 - lo: unclipped (min picks r A), gradient A r
+    loss, w, cl = orc.policy_terms([np.log(0.5)], [0.0], [2.0], lo, hi)
+    assert not cl[0] and w[0] == pytest.approx(1.0) and loss[0] == pytest.approx(-1.0)
+    # A < 0, r below 1 - lo: clipped; r above 1 + hi: unclipped
+    loss, w, cl = orc.policy_terms([np.log(0.5), np.log(1.5)], [0.0, 0.0], [-1.0, -1.0], lo, hi)
+    assert cl[0] and w[0] == 0.0 and loss[0] == pytest.approx(0.8)
+    assert not cl[1] and w[1] == pytest.approx(-1.5) and loss[1] == pytest.approx(1.5)
+    # ignored tokens contribute nothing
+    loss, w, _ = orc.policy_terms([0.1], [0.0], [3.0], lo, hi, ignored=[True])
+    assert loss[0] == 0.0 and w[0] == 0.0
+
+
+def test_policy_weight_is_minus_dloss_dlogprob():
+    g = np.random.default_rng(3)
+    lp = g.normal(-3.0, 1.0, 200)
+    old = lp + g.uniform(-0.5, 0.5, 200)
+    A = g.normal(0.0, 1.0, 200)
+    c = g.uniform(0.1, 1.0, 200)
+    h = 1e-7
+    lp_p, _, _ = orc.policy_terms(lp + h, old, A, 0.2, 0.28, c)
+    lp_m, _, _ = orc.policy_terms(lp - h, old, A, 0.2, 0.28, c)
+    _, w, cl = orc.policy_terms(lp, old, A, 0.2, 0.28, c)
+    r = np.exp(lp - old)
+    far = (np.abs(r - 0.8) > 1e-4) & (np.abs(r - 1.28) > 1e-4)
+    fd = -(lp_p - lp_m) / (2 * h)
+    np.testing.assert_allclose(w[far], fd[far], rtol=1e-6, atol=1e-9)
+
+
+def test_policy_gradient_through_the_softmax():
+    # d loss / d z = w (p - onehot) with w from policy_terms: finite differences
+    g = np.random.default_rng(5)
+    V, y = 9, 4
+    z = g.standard_normal(V) * 2
+    old, A, c = -1.7, 0.8, 0.3
+
+    def loss_of(zz):
+        lp, _, _ = fwd1(zz, y)
+        return orc.policy_terms([lp], [old], [A], 0.2, 0.28, [c])[0][0]
+
+    lp, _, lse = fwd1(z, y)
+    _, w, _ = orc.policy_terms([lp], [old], [A], 0.2, 0.28, [c])
+    grad = orc.backward(z[None, :], np.array([y]), np.array([lse]), w)[0]
+    for j in range(V):
+        zp, zm = z.copy(), z.copy()
+        zp[j] += 1e-6
+        zm[j] -= 1e-6
+        assert grad[j] == pytest.approx((loss_of(zp) - loss_of(zm)) / 2e-6, abs=1e-8)
