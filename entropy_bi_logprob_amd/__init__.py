@@ -22,7 +22,8 @@ import torch  # first: the library then binds to the HIP runtime torch has loade
 
 __all__ = [
     "IGNORE_INDEX", "BiError", "fwd", "bwd", "fwd_bwd", "policy_loss_fwd_bwd", "vocab_chunk_stats", "stats_combine",
-    "row_geometry", "LogprobEntropy", "logprob_entropy", "lib", "library_path",
+    "row_geometry", "fwd_multi", "diff_stats", "LogprobEntropy", "logprob_entropy", "lib",
+    "library_path",
 ]
 
 IGNORE_INDEX = -100
@@ -83,11 +84,15 @@ def lib() -> ctypes.CDLL:
     L.bi_policy_loss_fwd_bwd.argtypes = [vp, i32, i64, i64, i64, vp, i64, vp, vp, vp, f32, f32,
                                          vp, vp, vp, vp, vp, vp, i32, i64, vp, vp]
     L.bi_vocab_chunk_stats.argtypes = [vp, i32, i64, i64, i64, i64, i64, vp, i64, vp, vp, vp]
+    L.bi_logprob_fwd_multi.argtypes = [vp, i32, i64, i64, i64, vp, i64, i64, i64, vp, vp, vp,
+                                       vp, vp]
+    L.bi_logprob_diff_stats.argtypes = [vp, vp, vp, i64, i64, vp, vp]
     L.bi_stats_combine.argtypes = [vp, i64, i64, vp, i64, vp, vp, vp, vp]
     L.bi_row_geometry.argtypes = [i32, i64, ctypes.POINTER(i32), ctypes.POINTER(i32),
                                   ctypes.POINTER(i32)]
     for fn in ("bi_logprob_fwd", "bi_logprob_bwd", "bi_logprob_fwd_bwd",
-               "bi_policy_loss_fwd_bwd", "bi_vocab_chunk_stats",
+               "bi_policy_loss_fwd_bwd", "bi_vocab_chunk_stats", "bi_logprob_fwd_multi",
+               "bi_logprob_diff_stats",
                "bi_stats_combine", "bi_row_geometry"):
         getattr(L, fn).restype = i32
     L.bi_status_string.argtypes = [i32]
@@ -289,6 +294,38 @@ def stats_combine(stats: torch.Tensor, labels: torch.Tensor, ignore_index: int =
         _ptr(stats), c, n, _ptr(labels), ignore_index, _ptr(lp), _ptr(ent), _ptr(lse),
         _stream(stream)))
     return lp, ent, lse
+
+
+def fwd_multi(logits: torch.Tensor, labels: torch.Tensor, ignore_index: int = IGNORE_INDEX, *,
+              status: Optional[torch.Tensor] = None, stream=None):
+    """(logprob [N, K], entropy [N], lse [N]) for K token ids per row (labels [N, K])."""
+    n, v, rs = _rows(logits, "logits")
+    if labels.dim() != 2 or labels.shape[0] != n or labels.dtype != torch.int64 \
+            or not labels.is_cuda or (labels.shape[1] > 1 and labels.stride(1) != 1):
+        raise ValueError("labels must be a device int64 [N, K] tensor, last dim contiguous")
+    k = labels.shape[1]
+    _vec(status, 1, torch.int32, "status")
+    lp = torch.empty((n, k), dtype=torch.float32, device=logits.device)
+    ent = torch.empty(n, dtype=torch.float32, device=logits.device)
+    lse = torch.empty(n, dtype=torch.float32, device=logits.device)
+    ls = labels.stride(0) if n > 1 else k
+    _check("bi_logprob_fwd_multi", lib().bi_logprob_fwd_multi(
+        _ptr(logits), _dtype_code(logits.dtype), n, v, rs, _ptr(labels), ls, k, ignore_index,
+        _ptr(lp), _ptr(ent), _ptr(lse), _ptr(status), _stream(stream)))
+    return lp, ent, lse
+
+
+def diff_stats(a: torch.Tensor, b: torch.Tensor, labels: Optional[torch.Tensor] = None,
+               ignore_index: int = IGNORE_INDEX, stream=None) -> torch.Tensor:
+    """[4] fp32: mean (a-b), mean |a-b|, max |a-b|, fraction of tokens whose bits differ."""
+    n = a.shape[0] if a.dim() == 1 else -1
+    _vec(a, n, torch.float32, "a")
+    _vec(b, n, torch.float32, "b")
+    _vec(labels, n, torch.int64, "labels")
+    out = torch.empty(4, dtype=torch.float32, device=a.device)
+    _check("bi_logprob_diff_stats", lib().bi_logprob_diff_stats(
+        _ptr(a), _ptr(b), _ptr(labels), ignore_index, n, _ptr(out), _stream(stream)))
+    return out
 
 
 def row_geometry(dtype: torch.dtype, width: int) -> Tuple[int, int, int]:

@@ -837,6 +837,118 @@ void fused_reread_kernel(FusedArgs p) {
   }
 }
 
+// ------------------------------------------------ several labels per row
+//
+// The generator side of trainer/generator parity: K token ids per row share
+// one lse.  The scan, reduction and lse are exactly bi_logprob_fwd's, so the
+// column that holds a row's label carries the same bits as bi_logprob_fwd.
+
+struct MultiArgs {
+  const char* logits;
+  int64_t n_rows, vocab, row_bytes;
+  const int64_t* labels;
+  int64_t label_stride, k, ignore_index;
+  float* logprob;            // [n_rows, k]
+  float* entropy;
+  float* lse;
+  int32_t* status_flag;
+};
+
+template <int DT, bool ALIGNED>
+__global__ __launch_bounds__(kMaxThreads) __attribute__((amdgpu_waves_per_eu(8)))
+void fwd_multi_kernel(MultiArgs p) {
+  __shared__ float lds[3 * kMaxWaves + 1];
+  const int T = blockDim.x, tid = threadIdx.x;
+  for (int64_t row = blockIdx.x; row < p.n_rows; row += gridDim.x) {
+    const char* rp = p.logits + row * p.row_bytes;
+    const int64_t* yrow = p.labels + row * p.label_stride;
+    // the first T label logits are fetched before the scan
+    int64_t y0 = p.ignore_index;
+    float z0 = 0.0f;
+    if (tid < p.k) {
+      y0 = yrow[tid];
+      if (y0 != p.ignore_index && y0 >= 0 && y0 < p.vocab) z0 = Elt<DT>::load1(rp, y0);
+    }
+    Acc a = acc_empty();
+    const RowSrc src = row_src(rp, p.vocab * (DT == BI_BF16 ? 2 : 4), T, tid);
+    if (ALIGNED || (reinterpret_cast<uintptr_t>(rp) & 3u) == 0) {
+      row_scan<DT, true>(a, src, p.vocab, T, tid);
+    } else {
+      row_scan<DT, false>(a, src, p.vocab, T, tid);
+    }
+    const Acc r = block_reduce(a, lds, T, tid);
+    if (tid == 0) {
+      const float l = lse_of(r);
+      if (p.lse) p.lse[row] = l;
+      if (p.entropy) p.entropy[row] = entropy_of(r);
+      lds[3 * kMaxWaves] = l;
+    }
+    __syncthreads();
+    const float lse = lds[3 * kMaxWaves];
+    for (int64_t j = tid; j < p.k; j += T) {
+      const int64_t y = j == tid ? y0 : yrow[j];
+      const bool ignored = y == p.ignore_index;
+      const bool bad = !ignored && (y < 0 || y >= p.vocab);
+      float zy = j == tid ? z0 : 0.0f;
+      if (j != tid && !ignored && !bad) zy = Elt<DT>::load1(rp, y);
+      if (bad && p.status_flag) atomicOr(p.status_flag, BI_FLAG_BAD_LABEL);
+      p.logprob[row * p.k + j] = bad ? NAN : (ignored ? 0.0f : zy - lse);
+    }
+    if (row + gridDim.x < p.n_rows) __syncthreads();
+  }
+}
+
+// ------------------------------------ trainer-vs-generator difference metrics
+//
+// One workgroup: each lane sums its strided tokens in fp64, then a fixed tree
+// over the lanes; out = (mean d, mean |d|, max |d|, fraction of tokens whose
+// bits differ) with d = a - b over tokens whose label is not ignore_index.
+
+constexpr int kDiffThreads = 1024;
+
+__global__ __launch_bounds__(kDiffThreads) void diff_stats_kernel(
+    const float* a, const float* b, const int64_t* labels, int64_t ignore_index, int64_t n,
+    float* out) {
+  __shared__ double sd[kDiffThreads], sa[kDiffThreads];
+  __shared__ float sm[kDiffThreads];
+  __shared__ int64_t sc[kDiffThreads], sx[kDiffThreads];
+  const int tid = threadIdx.x;
+  double d_sum = 0.0, a_sum = 0.0;
+  float mx = 0.0f;
+  int64_t cnt = 0, differ = 0;
+  for (int64_t i = tid; i < n; i += kDiffThreads) {
+    if (labels && labels[i] == ignore_index) continue;
+    const float x = a[i], y = b[i];
+    const double d = double(x) - double(y);
+    d_sum += d;
+    a_sum += fabs(d);
+    const float ad = fabsf(x - y);
+    mx = (ad > mx || ad != ad) ? ad : mx;   // NaN sticks
+    cnt += 1;
+    differ += __float_as_uint(x) != __float_as_uint(y);
+  }
+  sd[tid] = d_sum; sa[tid] = a_sum; sm[tid] = mx; sc[tid] = cnt; sx[tid] = differ;
+  __syncthreads();
+  for (int w = kDiffThreads / 2; w > 0; w >>= 1) {
+    if (tid < w) {
+      sd[tid] += sd[tid + w];
+      sa[tid] += sa[tid + w];
+      const float o = sm[tid + w];
+      sm[tid] = (o > sm[tid] || o != o) ? o : sm[tid];
+      sc[tid] += sc[tid + w];
+      sx[tid] += sx[tid + w];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    const double c = double(sc[0]);
+    out[0] = sc[0] ? float(sd[0] / c) : 0.0f;
+    out[1] = sc[0] ? float(sa[0] / c) : 0.0f;
+    out[2] = sc[0] ? sm[0] : 0.0f;
+    out[3] = sc[0] ? float(double(sx[0]) / c) : 0.0f;
+  }
+}
+
 // One thread per row; chunks in ascending order (natural units).
 __global__ __launch_bounds__(256) void combine_kernel(const bi_stats* stats, int64_t n_chunks,
                                                       int64_t n_rows, const int64_t* labels,
@@ -1120,6 +1232,55 @@ int bi_policy_loss_fwd_bwd(const void* logits, int dtype, int64_t n_rows, int64_
               0, 0, labels, ignore_index, nullptr, logprob, entropy, lse, status_flag,
               old_logprob, advantages, loss_scale, clip_low, clip_high, loss, weight};
   return launch_fused<true>(fn, a, dtype, grad_dtype, row_stride, grad_row_stride, stream);
+}
+
+int bi_logprob_fwd_multi(const void* logits, int dtype, int64_t n_rows, int64_t vocab,
+                         int64_t row_stride, const int64_t* labels, int64_t label_stride,
+                         int64_t k, int64_t ignore_index, float* logprob, float* entropy,
+                         float* lse, int32_t* status_flag, bi_stream_t stream) {
+  const char* fn = "bi_logprob_fwd_multi";
+  if (int r = check_dtype(dtype, fn)) return r;
+  if (n_rows < 0) return fail(BI_ERR_SHAPE, "%s: n_rows %lld < 0", fn, (long long)n_rows);
+  if (vocab < 1 || vocab >= kMaxWidth)
+    return fail(BI_ERR_SHAPE, "%s: vocab %lld outside [1, 2^29)", fn, (long long)vocab);
+  if (row_stride < vocab)
+    return fail(BI_ERR_SHAPE, "%s: row_stride %lld < vocab %lld", fn, (long long)row_stride,
+                (long long)vocab);
+  if (k < 1 || label_stride < k)
+    return fail(BI_ERR_SHAPE, "%s: need 1 <= k <= label_stride (k %lld, stride %lld)", fn,
+                (long long)k, (long long)label_stride);
+  if (n_rows == 0) return ok();
+  if (!logits || !labels || !logprob)
+    return fail(BI_ERR_NULL, "%s: logits, labels and logprob are required", fn);
+  if (!aligned(logits, elem_size(dtype)) || !aligned(labels, 8) || !aligned(logprob, 4) ||
+      !aligned(entropy, 4) || !aligned(lse, 4) || !aligned(status_flag, 4))
+    return fail(BI_ERR_ALIGN, "%s: misaligned pointer", fn);
+  MultiArgs a{static_cast<const char*>(logits), n_rows, vocab, row_stride * int64_t(elem_size(dtype)),
+              labels, label_stride, k, ignore_index, logprob, entropy, lse, status_flag};
+  const Geometry g = row_geometry(dtype, vocab);
+  const dim3 grid(grid_for(n_rows)), block(g.threads);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool al = dtype == BI_F32 || rows_dword_aligned(logits, a.row_bytes);
+  if (dtype == BI_BF16) {
+    if (al) hipLaunchKernelGGL((fwd_multi_kernel<BI_BF16, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((fwd_multi_kernel<BI_BF16, false>), grid, block, 0, s, a);
+  } else {
+    hipLaunchKernelGGL((fwd_multi_kernel<BI_F32, true>), grid, block, 0, s, a);
+  }
+  return launched(fn);
+}
+
+int bi_logprob_diff_stats(const float* a, const float* b, const int64_t* labels,
+                          int64_t ignore_index, int64_t n, float* out, bi_stream_t stream) {
+  const char* fn = "bi_logprob_diff_stats";
+  if (n < 0) return fail(BI_ERR_SHAPE, "%s: n %lld < 0", fn, (long long)n);
+  if (!out) return fail(BI_ERR_NULL, "%s: out is required", fn);
+  if (n > 0 && (!a || !b)) return fail(BI_ERR_NULL, "%s: a and b are required", fn);
+  if (!aligned(a, 4) || !aligned(b, 4) || !aligned(labels, 8) || !aligned(out, 4))
+    return fail(BI_ERR_ALIGN, "%s: misaligned pointer", fn);
+  hipLaunchKernelGGL(diff_stats_kernel, dim3(1), dim3(kDiffThreads), 0,
+                     static_cast<hipStream_t>(stream), a, b, labels, ignore_index, n, out);
+  return launched(fn);
 }
 
 int bi_stats_combine(const bi_stats* stats, int64_t n_chunks, int64_t n_rows,

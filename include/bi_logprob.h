@@ -220,6 +220,34 @@ BI_API int bi_stats_combine(const bi_stats* stats, int64_t n_chunks, int64_t n_r
                      const int64_t* labels, int64_t ignore_index,
                      float* logprob, float* entropy, float* lse, bi_stream_t stream);
 
+/* Several token ids per row sharing one lse: the generator's
+ * compute_logprobs(logits, labels) with multi-column token ids (PR #4685,
+ * Correctness and compatibility).  lse and entropy are bit-identical to
+ * bi_logprob_fwd, and so is every column whose label equals the row's label.
+ *   labels       [n_rows, label_stride] int64; columns [0, k) are used
+ *   k            >= 1 token ids per row
+ *   logprob      [n_rows, k] fp32 (row-major, contiguous), required:
+ *                z[y] - lse, +0.0 for ignore_index, NaN for a bad id
+ *   entropy, lse [n_rows] fp32, each may be NULL
+ */
+BI_API int bi_logprob_fwd_multi(const void* logits, int dtype, int64_t n_rows, int64_t vocab,
+                                int64_t row_stride, const int64_t* labels, int64_t label_stride,
+                                int64_t k, int64_t ignore_index, float* logprob, float* entropy,
+                                float* lse, int32_t* status_flag, bi_stream_t stream);
+
+/* Trainer-vs-generator logprob difference metrics ("torchtitan-batch-
+ * invarient-GDN", Code map and Result: bit_wise logprob_diff mean / abs_mean
+ * / max and ratio_tokens_different).  With d = a - b over the tokens whose
+ * label is not ignore_index (all tokens when labels is NULL):
+ *   out[0] = mean d, out[1] = mean |d|, out[2] = max |d|,
+ *   out[3] = fraction of tokens whose fp32 bit patterns differ.
+ * Sums run in fp64 in a fixed order; no valid token gives zeros.
+ *   a, b   [n] fp32 device vectors; labels [n] int64 or NULL; out [4] fp32
+ */
+BI_API int bi_logprob_diff_stats(const float* a, const float* b, const int64_t* labels,
+                                 int64_t ignore_index, int64_t n, float* out,
+                                 bi_stream_t stream);
+
 /* Human-readable name of a status code (static string). */
 BI_API const char* bi_status_string(int status);
 

@@ -252,6 +252,53 @@ def combine(stats: np.ndarray, labels: np.ndarray, vocab: int,
 
 
 # ---------------------------------------------------------------------------
+# several label columns per row, and trainer-vs-generator difference metrics
+# ("[RL] Avoid full-vocab gather ...", Correctness and compatibility: the
+#  generator's compute_logprobs(logits, labels) with multi-column token ids;
+#  "torchtitan-batch-invarient-GDN", Code map and Result: the bit_wise
+#  logprob_diff mean / abs_mean / max and ratio_tokens_different metrics)
+# ---------------------------------------------------------------------------
+
+def forward_multi(z: np.ndarray, labels: np.ndarray, ignore_index: int = IGNORE_INDEX):
+    """logprob [n, K] = z[i, y_ik] - lse_i for every label column; plus entropy, lse."""
+    z = _as2d(z)
+    labels = np.asarray(labels, dtype=np.int64)
+    n, v = z.shape
+    m, S, U = row_statistics(z)
+    kind = label_kind(labels, v, ignore_index)
+    idx = np.where(kind == 0, labels, 0)
+    t = np.take_along_axis(z, idx, axis=1)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        lse = m + np.log(S)
+        entropy = np.log(S) - U / S
+        lp = np.where(kind == 1, 0.0, t - lse[:, None])
+    lp = np.where(kind == 2, np.nan, lp)
+    return lp, entropy, lse
+
+
+def diff_stats(a, b, labels=None, ignore_index: int = IGNORE_INDEX, a_bits=None, b_bits=None):
+    """(mean, abs_mean, max_abs, ratio_different) of d = a - b over valid tokens.
+
+    A token is valid unless its label is ignore_index.  ratio_different counts
+    tokens whose values differ bit for bit (bit patterns passed as uint32, or
+    compared as float32 values when not given).  No valid token gives zeros.
+    """
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    valid = np.ones(a.shape, dtype=bool) if labels is None else \
+        (np.asarray(labels, dtype=np.int64) != ignore_index)
+    if not valid.any():
+        return 0.0, 0.0, 0.0, 0.0
+    d = (a - b)[valid]
+    if a_bits is None:
+        a_bits = np.asarray(a, dtype=np.float32).view(np.uint32)
+        b_bits = np.asarray(b, dtype=np.float32).view(np.uint32)
+    differ = (np.asarray(a_bits) != np.asarray(b_bits))[valid]
+    return (float(d.sum() / d.size), float(np.abs(d).sum() / d.size),
+            float(np.abs(d).max()), float(differ.sum() / d.size))
+
+
+# ---------------------------------------------------------------------------
 # clipped-ratio policy loss per token (the weight of the fused backward)
 # ("torchtitan-batch-invarient-GDN", MATH recipe: DAPO with clip (0.2, 0.28);
 #  "[RL] Avoid full-vocab gather ...", Summary: per-token gradients for

@@ -35,7 +35,8 @@ def declared_functions():
 def test_header_declares_the_four_entry_points():
     names = declared_functions()
     for fn in ("bi_logprob_fwd", "bi_logprob_bwd", "bi_vocab_chunk_stats", "bi_stats_combine",
-               "bi_logprob_fwd_bwd", "bi_policy_loss_fwd_bwd"):
+               "bi_logprob_fwd_bwd", "bi_policy_loss_fwd_bwd", "bi_logprob_fwd_multi",
+               "bi_logprob_diff_stats"):
         assert fn in names
 
 
@@ -124,6 +125,19 @@ def test_policy_argument_errors(L):
     assert policy(L, adv=NUL) == bi.BI_ERR_NULL
     assert policy(L, loss=ctypes.c_void_p(0x10002)) == bi.BI_ERR_ALIGN
     assert policy(L, n=0, old=NUL, adv=NUL) == bi.BI_OK
+
+
+def test_multi_and_diff_argument_errors(L):
+    m = L.bi_logprob_fwd_multi
+    assert m(P, bi.BI_BF16, 4, 100, 100, P, 3, 4, -100, P, NUL, NUL, NUL, NUL) == bi.BI_ERR_SHAPE
+    assert m(P, bi.BI_BF16, 4, 100, 100, P, 4, 0, -100, P, NUL, NUL, NUL, NUL) == bi.BI_ERR_SHAPE
+    assert m(P, bi.BI_BF16, 4, 100, 100, P, 4, 4, -100, NUL, NUL, NUL, NUL, NUL) == bi.BI_ERR_NULL
+    assert m(P, 9, 4, 100, 100, P, 4, 4, -100, P, NUL, NUL, NUL, NUL) == bi.BI_ERR_DTYPE
+    d = L.bi_logprob_diff_stats
+    assert d(P, P, NUL, -100, -1, P, NUL) == bi.BI_ERR_SHAPE
+    assert d(P, P, NUL, -100, 10, NUL, NUL) == bi.BI_ERR_NULL
+    assert d(NUL, P, NUL, -100, 10, P, NUL) == bi.BI_ERR_NULL
+    assert d(P, P, ctypes.c_void_p(0x10004), -100, 10, P, NUL) == bi.BI_ERR_ALIGN
 
 
 def chunk(L, logits=P, dtype=bi.BI_BF16, n=4, w=25, rs=100, off=25, v=100, labels=P,

@@ -333,3 +333,65 @@ def test_policy_loss_against_oracle_and_two_calls(dt, V):
         assert w[i] == 0.0 or abs(w[i] - scale[i] * adv[i] * r[i]) <= 1e-5
     assert np.all(w[ign] == 0) and np.all(loss[ign] == 0)
     assert 0 < ocl[~ign].sum() < (~ign).sum()        # both branches are exercised
+
+
+@pytest.mark.parametrize("dt,V,K", [("bf16", 151_936, 5), ("f32", 20_011, 1), ("bf16", 4097, 1300)])
+def test_fwd_multi_columns(dt, V, K):
+    n = 9
+    b = random_batch(n, V, dt, seed=V + K, ignore_frac=0.0, mask_frac=0.05)
+    g = np.random.default_rng([V, K])
+    ids = g.integers(0, V, size=(n, K)).astype(np.int64)
+    ids[:, 0] = b.labels                      # column 0 holds the row's label
+    if K > 1:
+        ids[1, -1] = -100
+    if K > 2:
+        ids[2, 1] = V + 3                     # one bad id
+    logits = dev_logits(b.logits, dt)
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    lp, ent, lse = bi.fwd_multi(logits, dev(ids), status=flag)
+    lp1, ent1, lse1 = bi.fwd(logits, dev(b.labels))
+    torch.cuda.synchronize()
+    assert torch.equal(lse.view(torch.int32), lse1.view(torch.int32))
+    assert torch.equal(ent.view(torch.int32), ent1.view(torch.int32))
+    assert torch.equal(lp[:, 0].contiguous().view(torch.int32), lp1.view(torch.int32))
+    assert int(flag.item()) == (bi.BI_FLAG_BAD_LABEL if K > 2 else 0)
+    olp, oent, olse = orc.forward_multi(orc.decode(b.logits, dt), ids)
+    assert_close(host(lp), olp, TOL[dt][0], "multi logprob")
+    h = host(lp)
+    if K > 1:
+        assert h[1, -1] == 0.0 and not np.signbit(h[1, -1])
+
+
+def test_diff_stats_against_oracle():
+    g = np.random.default_rng(4)
+    n = 50_001
+    a = g.standard_normal(n).astype(np.float32)
+    b = a.copy()
+    idx = g.choice(n, 7_000, replace=False)
+    b[idx] += g.standard_normal(7_000).astype(np.float32) * 1e-3
+    labels = g.integers(0, 100, n).astype(np.int64)
+    labels[g.choice(n, 500, replace=False)] = -100
+    out = host(bi.diff_stats(dev(a), dev(b), dev(labels)))
+    want = orc.diff_stats(a, b, labels)
+    np.testing.assert_allclose(out[:2], want[:2], rtol=1e-6, atol=1e-12)
+    assert out[2] == np.float32(want[2]) and out[3] == np.float32(want[3])
+    zero = host(bi.diff_stats(dev(a), dev(a)))
+    assert np.all(zero == 0)
+
+
+def test_trainer_and_generator_logprobs_are_bitwise_equal():
+    # trainer: one call over a batch of 512 rows; generator: the same rows one at
+    # a time through the multi-column path with the label in column 3
+    b = random_batch(512, 151_936, "bf16", seed=77, ignore_frac=0.05)
+    logits, labels = dev_logits(b.logits, "bf16"), dev(b.labels)
+    pi, _, _ = bi.fwd(logits, labels)
+    g = np.random.default_rng(5)
+    mu = torch.empty_like(pi)
+    for i in range(0, 512, 37):
+        ids = g.integers(0, 151_936, size=(1, 6)).astype(np.int64)
+        ids[0, 3] = b.labels[i]
+        lp, _, _ = bi.fwd_multi(logits[i:i + 1], dev(ids))
+        mu[i] = lp[0, 3]
+    rows = torch.arange(0, 512, 37, device="cuda")
+    stats = host(bi.diff_stats(pi[rows].contiguous(), mu[rows].contiguous(), labels[rows].contiguous()))
+    assert np.all(stats == 0), stats

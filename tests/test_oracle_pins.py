@@ -542,3 +542,36 @@ def test_policy_gradient_through_the_softmax():
         zp[j] += 1e-6
         zm[j] -= 1e-6
         assert grad[j] == pytest.approx((loss_of(zp) - loss_of(zm)) / 2e-6, abs=1e-8)
+
+
+# ------------------------------------------- label columns and diff metrics
+
+def test_forward_multi_against_brute_force():
+    g = np.random.default_rng(12)
+    V = 11
+    z = g.standard_normal((3, V)) * 2
+    z[1, 3] = -np.inf
+    labels = np.array([[0, 5, 10, -100], [2, 2, 7, 1], [9, -100, 4, 0]])
+    lp, ent, lse = orc.forward_multi(z, labels)
+    for i in range(3):
+        for k in range(4):
+            blp, bh, blse, _ = orc.brute_force(z[i], int(labels[i, k]))
+            assert lp[i, k] == pytest.approx(blp, abs=1e-13)
+            assert ent[i] == pytest.approx(bh, abs=1e-13) and lse[i] == pytest.approx(blse, abs=1e-13)
+    assert lp[0, 3] == 0.0 and not np.signbit(lp[0, 3])
+    lp_bad, _, _ = orc.forward_multi(z, np.array([[V, -1, 0, 0]] * 3))
+    assert np.isnan(lp_bad[:, :2]).all() and np.isfinite(lp_bad[:, 2:]).all()
+
+
+def test_diff_stats_closed_cases():
+    a = np.array([1.0, 2.0, 3.0, 4.0], dtype=np.float32)
+    assert orc.diff_stats(a, a) == (0.0, 0.0, 0.0, 0.0)
+    b = np.array([1.0, 2.5, 3.0, 3.0], dtype=np.float32)
+    mean, amean, mx, ratio = orc.diff_stats(a, b)
+    assert mean == pytest.approx((0 - 0.5 + 0 + 1.0) / 4) and amean == pytest.approx(1.5 / 4)
+    assert mx == 1.0 and ratio == 0.5
+    # ignored tokens do not count; -0.0 and +0.0 differ bit for bit
+    mean, amean, mx, ratio = orc.diff_stats(np.array([0.0, 5.0], np.float32),
+                                            np.array([-0.0, 1.0], np.float32), [3, -100])
+    assert (mean, amean, mx, ratio) == (0.0, 0.0, 0.0, 1.0)
+    assert orc.diff_stats(a, b, [-100] * 4) == (0.0, 0.0, 0.0, 0.0)
