@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--cpu-sample-rows", type=int, default=4096)
     ap.add_argument("--profile-steps", type=int, default=None,
                     help="run only this many steps (for profilers); still prints the line")
+    ap.add_argument("--no-lmhead", action="store_true",
+                    help="skip the lm_head-projection leg (GEMM + statistics on matrix cores)")
     ap.add_argument("--calibrate-copy-gib", type=float, default=0.0,
                     help="first run one plain elementwise copy of this many GiB (bf16 in, "
                          "bf16 out), a known-size reference for memory counters")
@@ -73,6 +75,57 @@ def measured_traffic(kernel):
     if block.get("source_sha256") != sha or kernel not in block.get("per_launch", {}):
         return None
     return block["per_launch"][kernel]["traffic_bytes"]
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
+
+
+def lmhead_leg(bi, torch, np, wl, N, V, seed, steps, warm, stream):
+    """Logprob/entropy straight from hidden states: hidden [N, 2560] x lm_head [V, 2560]^T
+    on the matrix cores, reduced to statistics without materialising the logits; timed
+    beside the unfused pipeline (library GEMM to bf16 logits, then bi_logprob_fwd)."""
+    d = wl.LMHEAD_HIDDEN
+    b = wl.lmhead_batch(N, V, d, seed=seed)
+    dev = torch.device("cuda:0")
+    H = torch.from_numpy(b.hidden.view(np.int16)).to(dev).view(torch.bfloat16)
+    W = torch.from_numpy(b.weight.view(np.int16)).to(dev).view(torch.bfloat16)
+    labels = torch.from_numpy(b.labels).to(dev)
+    tiles = int(bi.lib().bi_lmhead_tiles(V))
+    st = torch.empty((tiles, N, 4), dtype=torch.float32, device=dev)
+    outs = tuple(torch.empty(N, dtype=torch.float32, device=dev) for _ in range(3))
+    ks = max(1, min(steps, 10))
+
+    def timed(fns):
+        for _ in range(max(1, min(warm, 2))):
+            for f in fns:
+                f()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
+              for _ in range(ks)]
+        for k in range(ks):
+            ev[k][0].record(stream)
+            for i, f in enumerate(fns):
+                f()
+                ev[k][i + 1].record(stream)
+        torch.cuda.synchronize()
+        return [float(np.mean([e[i].elapsed_time(e[i + 1]) for e in ev])) for i in range(len(fns))]
+
+    t_stats, t_comb = timed([lambda: bi.lmhead_tile_stats(H, W, labels, out=st, stream=stream),
+                             lambda: bi.stats_combine(st, labels, out=outs, stream=stream)])
+    logits = torch.empty((N, V), dtype=torch.bfloat16, device=dev)
+    t_gemm, t_fwd = timed([lambda: torch.matmul(H, W.t(), out=logits),
+                           lambda: bi.fwd(logits, labels, out=outs, stream=stream)])
+    del logits, st
+    flops = 2.0 * N * V * d
+    tf = flops / (t_stats * 1e-3) / 1e12
+    return {"workload": f"hidden {N}x{d} bf16, lm_head {V}x{d} bf16",
+            "fused_ms": t_stats + t_comb, "tile_stats_ms": t_stats, "combine_ms": t_comb,
+            "rows_per_s": N / ((t_stats + t_comb) * 1e-3),
+            "roofline": {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": tf / MFMA_BF16_PEAK_TFLOPS, "traffic": None},
+            "unfused_ms": t_gemm + t_fwd, "unfused_gemm_ms": t_gemm, "unfused_fwd_ms": t_fwd,
+            "unfused_gemm_TFLOPs": flops / (t_gemm * 1e-3) / 1e12,
+            "speedup_vs_unfused": (t_gemm + t_fwd) / (t_stats + t_comb)}
 
 
 def cpu_baseline(rows_total, sample_rows, seed):
@@ -281,6 +334,8 @@ def main():
         "policy_loss": policy,
         "input_gen_s": gen_s,
     }
+    if not args.no_lmhead:
+        line["lmhead"] = lmhead_leg(bi, torch, np, wl, N, V, seed, steps, warm, stream)
     if not args.no_cpu_baseline and not args.profile_steps:
         line["cpu_baseline"] = cpu_baseline(N, args.cpu_sample_rows, seed)
     print(json.dumps(line), flush=True)

@@ -22,7 +22,8 @@ import torch  # first: the library then binds to the HIP runtime torch has loade
 
 __all__ = [
     "IGNORE_INDEX", "BiError", "fwd", "bwd", "fwd_bwd", "policy_loss_fwd_bwd", "vocab_chunk_stats", "stats_combine",
-    "row_geometry", "fwd_multi", "diff_stats", "LogprobEntropy", "logprob_entropy", "lib",
+    "row_geometry", "fwd_multi", "diff_stats", "lmhead_tile_stats", "lmhead_logprob",
+    "LogprobEntropy", "logprob_entropy", "lib",
     "library_path",
 ]
 
@@ -87,6 +88,11 @@ def lib() -> ctypes.CDLL:
     L.bi_logprob_fwd_multi.argtypes = [vp, i32, i64, i64, i64, vp, i64, i64, i64, vp, vp, vp,
                                        vp, vp]
     L.bi_logprob_diff_stats.argtypes = [vp, vp, vp, i64, i64, vp, vp]
+    L.bi_lmhead_tile_stats.argtypes = [vp, vp, i64, i64, i64, i64, i64, i64, i64, vp, i64, vp,
+                                       vp, vp]
+    L.bi_lmhead_tile_stats.restype = i32
+    L.bi_lmhead_tiles.argtypes = [i64]
+    L.bi_lmhead_tiles.restype = i64
     L.bi_stats_combine.argtypes = [vp, i64, i64, vp, i64, vp, vp, vp, vp]
     L.bi_row_geometry.argtypes = [i32, i64, ctypes.POINTER(i32), ctypes.POINTER(i32),
                                   ctypes.POINTER(i32)]
@@ -326,6 +332,42 @@ def diff_stats(a: torch.Tensor, b: torch.Tensor, labels: Optional[torch.Tensor] 
     _check("bi_logprob_diff_stats", lib().bi_logprob_diff_stats(
         _ptr(a), _ptr(b), _ptr(labels), ignore_index, n, _ptr(out), _stream(stream)))
     return out
+
+
+def lmhead_tile_stats(hidden: torch.Tensor, weight: torch.Tensor, labels: torch.Tensor,
+                      vocab_offset: int = 0, vocab: Optional[int] = None,
+                      ignore_index: int = IGNORE_INDEX, *, out: Optional[torch.Tensor] = None,
+                      status: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """[tiles, N, 4] statistics of hidden [N, d] @ weight[Vc, d]^T, by 128-row tiles.
+
+    ``weight`` holds the lm_head rows of global vocabulary ids
+    vocab_offset .. vocab_offset + Vc - 1; ``vocab`` is the global size
+    (defaults to vocab_offset + Vc).
+    """
+    n, d, ldh = _rows(hidden, "hidden")
+    vc, dw, ldw = _rows(weight, "weight")
+    if hidden.dtype != torch.bfloat16 or weight.dtype != torch.bfloat16 or d != dw:
+        raise ValueError("hidden [N, d] and weight [Vc, d] must be bfloat16 with the same d")
+    _vec(labels, n, torch.int64, "labels")
+    _vec(status, 1, torch.int32, "status")
+    vocab = vocab_offset + vc if vocab is None else vocab
+    tiles = int(lib().bi_lmhead_tiles(vc))
+    if out is None:
+        out = torch.empty((tiles, n, 4), dtype=torch.float32, device=hidden.device)
+    if out.shape != (tiles, n, 4) or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous float32 [{tiles}, {n}, 4] tensor")
+    _check("bi_lmhead_tile_stats", lib().bi_lmhead_tile_stats(
+        _ptr(hidden), _ptr(weight), n, vc, d, ldh, ldw, vocab_offset, vocab, _ptr(labels),
+        ignore_index, _ptr(out), _ptr(status), _stream(stream)))
+    return out
+
+
+def lmhead_logprob(hidden: torch.Tensor, weight: torch.Tensor, labels: torch.Tensor,
+                   ignore_index: int = IGNORE_INDEX, status=None, stream=None):
+    """(logprob, entropy, lse) of the logits hidden @ weight^T without materialising them."""
+    st = lmhead_tile_stats(hidden, weight, labels, 0, weight.shape[0], ignore_index,
+                           status=status, stream=stream)
+    return stats_combine(st, labels, ignore_index, stream=stream)
 
 
 def row_geometry(dtype: torch.dtype, width: int) -> Tuple[int, int, int]:

@@ -949,6 +949,226 @@ __global__ __launch_bounds__(kDiffThreads) void diff_stats_kernel(
   }
 }
 
+// ------------------------------------------------ lm_head GEMM + statistics
+//
+// The logits of a vocabulary chunk computed on the matrix cores from the
+// hidden states and the lm_head rows, and reduced at once to per-token
+// statistics, so the [N, V] logits never reach HBM (the chunked lm_head of
+// "ZeroSyncGRPOTrainer", with the shard-local statistics of PR #4685 Why).
+//
+// MFMA v_mfma_f32_32x32x16_bf16 with A = lm_head rows W[v, k] and B = hidden
+// rows H[n, k]: D[v][n] = sum_k W[v, k] H[n, k], so each lane holds one
+// token's column and the statistics of a token need no shuffles within a
+// 32 x 32 block (lane l: token l % 32, vocab rows 8*(r/4) + 4*(l/32) + r%4 of
+// accumulator r).  A workgroup of 4 waves owns a 128-vocab x 128-token tile
+// (each wave 64 x 64, i.e. 2 x 2 blocks) and runs over all of K in LDS stages
+// of 64, double-buffered.  Every logit is the same fixed sequence of MFMAs
+// over K whatever N is, so the statistics are batch-invariant.  The epilogue
+// folds the tile's 128 logits of each token into one bi_stats (fixed order:
+// the lane's 32 values, then the lane halves, then the two vocab waves),
+// written as "chunk" tv of the token; bi_stats_combine then reduces the
+// tiles in ascending order.
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kLmTile = 128;        // vocab rows and tokens per workgroup tile
+constexpr int kLmBK = 64;           // K per LDS stage
+constexpr int kLmRow = kLmBK + 8;   // LDS row pitch in bf16: 144 bytes spreads the banks
+constexpr int kLmThreads = 256;     // 4 waves: 2 (vocab) x 2 (tokens)
+
+struct LmArgs {
+  const uint16_t* hidden;   // [n_tok, ldh] bf16 bits
+  const uint16_t* weight;   // [n_voc, ldw] bf16 bits
+  int64_t n_tok, n_voc, d, ldh, ldw;
+  int64_t vocab_offset, vocab;
+  const int64_t* labels;
+  int64_t ignore_index;
+  bi_stats* stats;          // [tiles_v][n_tok]
+  int32_t* status_flag;
+  int64_t tiles_v, tiles_n;
+};
+
+// Tile of block b.  Workgroups go to the 8 XCDs round-robin; each XCD gets a
+// contiguous run of tiles, in which groups of 8 token tiles sweep the
+// vocabulary tiles together, so the W and H slices in flight are shared
+// through that XCD's L2.
+__device__ inline bool lm_tile_of(const LmArgs& p, int64_t b, int64_t* tv, int64_t* tn) {
+  const int64_t total = p.tiles_v * p.tiles_n;
+  const int64_t per_xcd = (total + 7) / 8;
+  const int64_t t = (b % 8) * per_xcd + b / 8;
+  if (t >= total) return false;
+  const int64_t group = t / (8 * p.tiles_v), r = t % (8 * p.tiles_v);
+  const int64_t rows_in_group = min(int64_t(8), p.tiles_n - group * 8);
+  *tn = group * 8 + r % rows_in_group;
+  *tv = r / rows_in_group;
+  return *tv < p.tiles_v;
+}
+
+struct LmStage {
+  u32x4 w[4], h[4];
+};
+
+__device__ inline void lm_load(const LmArgs& p, int64_t v0, int64_t n0, int64_t k0, int tid,
+                               LmStage& st) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = tid + kLmThreads * i;   // 0..1023: row q/8, 16-byte column q%8
+    const int row = q >> 3, kv = q & 7;
+    const int64_t v = v0 + row, n = n0 + row;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    st.w[i] = v < p.n_voc
+                  ? *reinterpret_cast<const u32x4*>(p.weight + v * p.ldw + k0 + 8 * kv)
+                  : zero;
+    st.h[i] = n < p.n_tok
+                  ? *reinterpret_cast<const u32x4*>(p.hidden + n * p.ldh + k0 + 8 * kv)
+                  : zero;
+  }
+}
+
+__device__ inline void lm_store(uint16_t* sW, uint16_t* sH, int tid, const LmStage& st) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = tid + kLmThreads * i;
+    const int row = q >> 3, kv = q & 7;
+    *reinterpret_cast<u32x4*>(sW + row * kLmRow + 8 * kv) = st.w[i];
+    *reinterpret_cast<u32x4*>(sH + row * kLmRow + 8 * kv) = st.h[i];
+  }
+}
+
+__device__ inline void lm_mma_stage(const uint16_t* sW, const uint16_t* sH, int wv, int wt,
+                                    int lane, f32x16 (&acc)[2][2]) {
+  const int lr = lane & 31, lk = 8 * (lane >> 5);
+#pragma unroll
+  for (int kk = 0; kk < kLmBK / 16; ++kk) {
+    bf16x8 a[2], b[2];
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      a[x] = *reinterpret_cast<const bf16x8*>(sW + (64 * wv + 32 * x + lr) * kLmRow + 16 * kk + lk);
+      b[x] = *reinterpret_cast<const bf16x8*>(sH + (64 * wt + 32 * x + lr) * kLmRow + 16 * kk + lk);
+    }
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int y = 0; y < 2; ++y)
+        acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[x], b[y], acc[x][y], 0, 0, 0);
+  }
+}
+
+// (m, c, S, U, t) of one token: a (+) b with a taken first
+__device__ inline void lm_merge(Acc& a, float& ta, const Acc& b, float tb) {
+  const float M = fmaxf(a.m, b.m);
+  const float C = ref_of(M);
+  Acc x = a, y = b;
+  rebase(x, C);
+  rebase(y, C);
+  a.m = M;
+  a.c = C;
+  a.S = x.S + y.S;
+  a.U = x.U + y.U;
+  ta = ta + tb;
+}
+
+__global__ __launch_bounds__(kLmThreads) void lmhead_stats_kernel(LmArgs p) {
+  __shared__ __attribute__((aligned(16))) uint16_t sW[2][kLmTile * kLmRow];
+  __shared__ __attribute__((aligned(16))) uint16_t sH[2][kLmTile * kLmRow];
+  __shared__ float red[2][2][32][4];
+  int64_t tv, tn;
+  if (!lm_tile_of(p, blockIdx.x, &tv, &tn)) return;   // whole workgroup exits together
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wv = wave & 1, wt = wave >> 1;
+  const int64_t v0 = tv * kLmTile, n0 = tn * kLmTile;
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[x][y][r] = 0.0f;
+
+  const int64_t stages = p.d / kLmBK;
+  LmStage st;
+  lm_load(p, v0, n0, 0, tid, st);
+  lm_store(sW[0], sH[0], tid, st);
+  __syncthreads();
+  for (int64_t s = 0; s + 1 < stages; ++s) {
+    lm_load(p, v0, n0, (s + 1) * kLmBK, tid, st);
+    lm_mma_stage(sW[s & 1], sH[s & 1], wv, wt, lane, acc);
+    lm_store(sW[(s + 1) & 1], sH[(s + 1) & 1], tid, st);
+    __syncthreads();
+  }
+  lm_mma_stage(sW[(stages - 1) & 1], sH[(stages - 1) & 1], wv, wt, lane, acc);
+
+  // epilogue: statistics of each token over this tile's 128 vocabulary rows
+#pragma unroll
+  for (int y = 0; y < 2; ++y) {
+    const int64_t j = n0 + 64 * wt + 32 * y + (lane & 31);
+    float z[32];
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t i = v0 + 64 * wv + 32 * x + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        z[16 * x + r] = i < p.n_voc ? acc[x][y][r] : -INFINITY;
+      }
+    Acc a = acc_empty();
+    accumulate<8, 4>(a, z);
+    // the label's logit, held by exactly one lane of one vocab wave (if here)
+    float t = 0.0f;
+    const int64_t lab = j < p.n_tok ? p.labels[j] : p.ignore_index;
+    const bool bad = lab != p.ignore_index && (lab < 0 || lab >= p.vocab);
+    const int64_t local = lab - p.vocab_offset;               // row within these lm_head rows
+    const int64_t yl = local - v0 - 64 * wv;                  // row within this wave's 64
+    if (!bad && lab != p.ignore_index && local < p.n_voc && yl >= 0 && yl < 64) {
+      const int x = int(yl >> 5), rr = int(yl & 31);
+      if ((lane >> 5) == ((rr >> 2) & 1)) {
+        const int r = (rr >> 3) * 4 + (rr & 3);
+#pragma unroll
+        for (int q = 0; q < 32; ++q)
+          if (q == 16 * x + r) t = z[q];
+      }
+    }
+    // lane halves (same token, other rows), lower half first
+    Acc o;
+    o.m = __shfl_xor(a.m, 32);
+    o.c = __shfl_xor(a.c, 32);
+    o.S = __shfl_xor(a.S, 32);
+    o.U = __shfl_xor(a.U, 32);
+    const float ot = __shfl_xor(t, 32);
+    Acc lo = (lane < 32) ? a : o, hi = (lane < 32) ? o : a;
+    float tlo = (lane < 32) ? t : ot, thi = (lane < 32) ? ot : t;
+    lm_merge(lo, tlo, hi, thi);
+    if (wv == 1 && lane < 32) {
+      red[wt][y][lane][0] = lo.m;
+      red[wt][y][lane][1] = lo.S;
+      red[wt][y][lane][2] = lo.U;
+      red[wt][y][lane][3] = tlo;
+    }
+    __syncthreads();
+    if (wv == 0 && lane < 32) {
+      Acc b;
+      b.m = red[wt][y][lane][0];
+      b.c = ref_of(b.m);
+      b.S = red[wt][y][lane][1];
+      b.U = red[wt][y][lane][2];
+      lm_merge(lo, tlo, b, red[wt][y][lane][3]);
+      if (j < p.n_tok) {
+        const float d = fmaf(lo.m, kLog2e, lo.c);
+        const float f = exp2_hw(-d);
+        bi_stats out;
+        out.max = lo.m;
+        out.sumexp = lo.S == 0.0f ? 0.0f : lo.S * f;
+        out.sumexp_logit = lo.S == 0.0f ? 0.0f : kLn2 * (fmaf(-d, lo.S, lo.U) * f);
+        out.target = bad ? NAN : tlo;
+        p.stats[tv * p.n_tok + j] = out;
+        if (bad && p.status_flag) atomicOr(p.status_flag, BI_FLAG_BAD_LABEL);
+      }
+    }
+    __syncthreads();
+  }
+}
+
 // One thread per row; chunks in ascending order (natural units).
 __global__ __launch_bounds__(256) void combine_kernel(const bi_stats* stats, int64_t n_chunks,
                                                       int64_t n_rows, const int64_t* labels,
@@ -1280,6 +1500,45 @@ int bi_logprob_diff_stats(const float* a, const float* b, const int64_t* labels,
     return fail(BI_ERR_ALIGN, "%s: misaligned pointer", fn);
   hipLaunchKernelGGL(diff_stats_kernel, dim3(1), dim3(kDiffThreads), 0,
                      static_cast<hipStream_t>(stream), a, b, labels, ignore_index, n, out);
+  return launched(fn);
+}
+
+int64_t bi_lmhead_tiles(int64_t n_vocab_rows) {
+  return n_vocab_rows <= 0 ? 0 : (n_vocab_rows + kLmTile - 1) / kLmTile;
+}
+
+int bi_lmhead_tile_stats(const void* hidden, const void* weight, int64_t n_tokens,
+                         int64_t n_vocab_rows, int64_t d, int64_t hidden_stride,
+                         int64_t weight_stride, int64_t vocab_offset, int64_t vocab,
+                         const int64_t* labels, int64_t ignore_index, bi_stats* stats,
+                         int32_t* status_flag, bi_stream_t stream) {
+  const char* fn = "bi_lmhead_tile_stats";
+  if (n_tokens < 0 || n_vocab_rows < 0)
+    return fail(BI_ERR_SHAPE, "%s: negative size", fn);
+  if (d < kLmBK || d % kLmBK != 0)
+    return fail(BI_ERR_SHAPE, "%s: d = %lld must be a positive multiple of %d", fn, (long long)d,
+                kLmBK);
+  if (hidden_stride < d || weight_stride < d || hidden_stride % 8 || weight_stride % 8)
+    return fail(BI_ERR_SHAPE, "%s: strides must be >= d and multiples of 8 elements", fn);
+  if (vocab < 1 || vocab_offset < 0 || vocab_offset + n_vocab_rows > vocab)
+    return fail(BI_ERR_SHAPE, "%s: rows [%lld, %lld) outside the vocabulary [0, %lld)", fn,
+                (long long)vocab_offset, (long long)(vocab_offset + n_vocab_rows),
+                (long long)vocab);
+  if (n_tokens == 0 || n_vocab_rows == 0) return ok();
+  if (!hidden || !weight || !labels || !stats)
+    return fail(BI_ERR_NULL, "%s: hidden, weight, labels and stats are required", fn);
+  if (!aligned(hidden, 16) || !aligned(weight, 16) || !aligned(labels, 8) ||
+      !aligned(stats, 16) || !aligned(status_flag, 4))
+    return fail(BI_ERR_ALIGN, "%s: hidden and weight need 16-byte alignment", fn);
+  LmArgs a{static_cast<const uint16_t*>(hidden), static_cast<const uint16_t*>(weight),
+           n_tokens, n_vocab_rows, d, hidden_stride, weight_stride, vocab_offset, vocab,
+           labels, ignore_index, stats, status_flag, bi_lmhead_tiles(n_vocab_rows),
+           (n_tokens + kLmTile - 1) / kLmTile};
+  const int64_t total = a.tiles_v * a.tiles_n;
+  const int64_t blocks = 8 * ((total + 7) / 8);
+  if (blocks > 0x7fffffff) return fail(BI_ERR_SHAPE, "%s: too many tiles", fn);
+  hipLaunchKernelGGL(lmhead_stats_kernel, dim3(unsigned(blocks)), dim3(kLmThreads), 0,
+                     static_cast<hipStream_t>(stream), a);
   return launched(fn);
 }
 

@@ -248,6 +248,32 @@ BI_API int bi_logprob_diff_stats(const float* a, const float* b, const int64_t* 
                                  int64_t ignore_index, int64_t n, float* out,
                                  bi_stream_t stream);
 
+/* lm_head projection fused with the chunk statistics: the logits
+ * z[n, v] = sum_k hidden[n, k] * weight[v, k] of a block of lm_head rows are
+ * computed on the matrix cores (bf16 inputs, fp32 accumulation) and reduced
+ * straight to bi_stats per token, so the logits never reach memory (the
+ * chunked lm_head of "ZeroSyncGRPOTrainer - #6949"; shard-local statistics,
+ * PR #4685 Why).  Rows are cut into tiles of 128; tile c of token n is
+ * written to stats[c * n_tokens + n], with the same meaning as
+ * bi_vocab_chunk_stats on those 128 columns.  bi_stats_combine over the
+ * bi_lmhead_tiles(n_vocab_rows) tiles then yields logprob, entropy and lse.
+ * Each logit is the same MFMA sequence whatever n_tokens is (batch-
+ * invariant).  The fp32 logits are used as computed (not rounded to bf16).
+ *   hidden  [n_tokens, hidden_stride] bf16, 16-byte aligned rows
+ *   weight  [n_vocab_rows, weight_stride] bf16 (the lm_head rows of global
+ *           vocabulary ids vocab_offset .. vocab_offset + n_vocab_rows - 1)
+ *   d       hidden size, a positive multiple of 64; strides multiples of 8
+ *   stats   [bi_lmhead_tiles(n_vocab_rows)][n_tokens] bi_stats, 16-byte aligned
+ */
+BI_API int bi_lmhead_tile_stats(const void* hidden, const void* weight, int64_t n_tokens,
+                                int64_t n_vocab_rows, int64_t d, int64_t hidden_stride,
+                                int64_t weight_stride, int64_t vocab_offset, int64_t vocab,
+                                const int64_t* labels, int64_t ignore_index, bi_stats* stats,
+                                int32_t* status_flag, bi_stream_t stream);
+
+/* Number of 128-row tiles bi_lmhead_tile_stats writes for n_vocab_rows rows. */
+BI_API int64_t bi_lmhead_tiles(int64_t n_vocab_rows);
+
 /* Human-readable name of a status code (static string). */
 BI_API const char* bi_status_string(int status);
 

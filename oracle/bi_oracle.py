@@ -252,6 +252,26 @@ def combine(stats: np.ndarray, labels: np.ndarray, vocab: int,
 
 
 # ---------------------------------------------------------------------------
+# lm_head projection fused with the statistics ("ZeroSyncGRPOTrainer" PR:
+# chunked lm_head over a replicated vocabulary projection; "[RL] Avoid
+# full-vocab gather ...", Why: shard-local statistics)
+# ---------------------------------------------------------------------------
+
+def lmhead_logits(hidden: np.ndarray, weight: np.ndarray) -> np.ndarray:
+    """logits [n, V] = hidden [n, d] @ weight[V, d]^T, exactly (float64 matmul)."""
+    return np.asarray(hidden, dtype=np.float64) @ np.asarray(weight, dtype=np.float64).T
+
+
+def lmhead_tile_stats(hidden, weight, labels, vocab_offset: int, vocab: int, tile: int,
+                      ignore_index: int = IGNORE_INDEX) -> np.ndarray:
+    """chunk_stats of each `tile`-row block of the lm_head rows -> [ceil(V_c / tile), n, 4]."""
+    z = lmhead_logits(hidden, weight)
+    vc = z.shape[1]
+    return np.stack([chunk_stats(z[:, a:min(a + tile, vc)], labels, vocab_offset + a, vocab,
+                                 ignore_index) for a in range(0, vc, tile)])
+
+
+# ---------------------------------------------------------------------------
 # several label columns per row, and trainer-vs-generator difference metrics
 # ("[RL] Avoid full-vocab gather ...", Correctness and compatibility: the
 #  generator's compute_logprobs(logits, labels) with multi-column token ids;

@@ -36,7 +36,7 @@ def test_header_declares_the_four_entry_points():
     names = declared_functions()
     for fn in ("bi_logprob_fwd", "bi_logprob_bwd", "bi_vocab_chunk_stats", "bi_stats_combine",
                "bi_logprob_fwd_bwd", "bi_policy_loss_fwd_bwd", "bi_logprob_fwd_multi",
-               "bi_logprob_diff_stats"):
+               "bi_logprob_diff_stats", "bi_lmhead_tile_stats", "bi_lmhead_tiles"):
         assert fn in names
 
 
@@ -138,6 +138,24 @@ def test_multi_and_diff_argument_errors(L):
     assert d(P, P, NUL, -100, 10, NUL, NUL) == bi.BI_ERR_NULL
     assert d(NUL, P, NUL, -100, 10, P, NUL) == bi.BI_ERR_NULL
     assert d(P, P, ctypes.c_void_p(0x10004), -100, 10, P, NUL) == bi.BI_ERR_ALIGN
+
+
+def test_lmhead_argument_errors(L):
+    f = L.bi_lmhead_tile_stats
+    args = dict(h=P, w=P, n=8, vc=300, d=128, ldh=128, ldw=128, off=0, v=300, lab=P, st=P)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["h"], a["w"], a["n"], a["vc"], a["d"], a["ldh"], a["ldw"], a["off"], a["v"],
+                 a["lab"], -100, a["st"], NUL, NUL)
+
+    assert call(d=100) == bi.BI_ERR_SHAPE        # not a multiple of 64
+    assert call(ldh=130) == bi.BI_ERR_SHAPE      # stride not a multiple of 8
+    assert call(off=10) == bi.BI_ERR_SHAPE       # rows past the vocabulary
+    assert call(h=NUL) == bi.BI_ERR_NULL
+    assert call(w=ctypes.c_void_p(0x10008)) == bi.BI_ERR_ALIGN
+    assert call(n=0, h=NUL, w=NUL, lab=NUL, st=NUL) == bi.BI_OK
+    assert L.bi_lmhead_tiles(300) == 3 and L.bi_lmhead_tiles(128) == 1 and L.bi_lmhead_tiles(0) == 0
 
 
 def chunk(L, logits=P, dtype=bi.BI_BF16, n=4, w=25, rs=100, off=25, v=100, labels=P,

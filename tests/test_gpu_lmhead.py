@@ -1,0 +1,103 @@
+"""GPU parity of the lm_head projection fused with the statistics.
+
+bi_lmhead_tile_stats computes the logits hidden @ weight^T on the matrix cores
+and reduces them to per-token statistics of 128-row tiles; bi_stats_combine
+finishes.  Checked against the fp64 oracle (exact float64 products of the bf16
+inputs): per-tile statistics, and the combined logprob / entropy / lse within
+2e-4 (the logits are fp32 accumulations of exact bf16 products, so the
+fp32-logits tolerance applies).  Also: ragged token and vocabulary tiles, tiles
+of a token that do not depend on the batch (bit for bit), and vocabulary
+shards that reproduce the unsharded tiles.
+"""
+import numpy as np
+import pytest
+import torch
+
+import entropy_bi_logprob_amd as bi
+import oracle.bi_oracle as orc
+import workloads as wl
+from gpu_util import assert_close, dev, host
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-4
+
+
+def to_dev_bf16(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def check_tiles(st, ost):
+    st = np.asarray(st, dtype=np.float64)
+    np.testing.assert_allclose(st[..., 0], ost[..., 0], rtol=0, atol=2e-5)          # max
+    np.testing.assert_allclose(st[..., 1], ost[..., 1], rtol=2e-5)                  # sumexp
+    np.testing.assert_allclose(st[..., 2], ost[..., 2], rtol=0, atol=2e-5)          # target
+    np.testing.assert_allclose(st[..., 3], ost[..., 3], rtol=2e-5, atol=2e-4)       # sumexp_logit
+
+
+@pytest.mark.parametrize("n,vc,d", [(300, 1000, 128), (128, 128, 64), (77, 333, 256),
+                                    (1000, 4099, 512), (5, 130, 64)])
+def test_tiles_and_combine_against_oracle(n, vc, d):
+    b = wl.lmhead_batch(n, vc, d, seed=n + vc + d, ignore_frac=0.1)
+    H, W, labels = to_dev_bf16(b.hidden), to_dev_bf16(b.weight), dev(b.labels)
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    st = bi.lmhead_tile_stats(H, W, labels, status=flag)
+    lp, ent, lse = bi.stats_combine(st, labels)
+    torch.cuda.synchronize()
+    assert int(flag.item()) == 0
+    h = orc.decode(b.hidden, "bf16")
+    w = orc.decode(b.weight, "bf16")
+    check_tiles(host(st), orc.lmhead_tile_stats(h, w, b.labels, 0, vc, 128))
+    olp, oent, olse = orc.forward(orc.lmhead_logits(h, w), b.labels)
+    assert_close(host(lp), olp, TOL, "logprob")
+    assert_close(host(ent), oent, TOL, "entropy")
+    assert_close(host(lse), olse, TOL, "lse")
+    ign = b.labels == -100
+    assert np.all(host(lp)[ign] == 0) and not np.any(np.signbit(host(lp)[ign]))
+
+
+def test_tiles_do_not_depend_on_the_batch():
+    n, vc, d = 640, 1500, 256
+    b = wl.lmhead_batch(n, vc, d, seed=3)
+    H, W, labels = to_dev_bf16(b.hidden), to_dev_bf16(b.weight), dev(b.labels)
+    full = bi.lmhead_tile_stats(H, W, labels)
+    idx = torch.tensor([5, 600, 129, 0, 333, 639, 64], device="cuda")
+    sub = bi.lmhead_tile_stats(H[idx].contiguous(), W, labels[idx].contiguous())
+    one = bi.lmhead_tile_stats(H[idx[1:2]].contiguous(), W, labels[idx[1:2]].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(full[:, idx].contiguous().view(torch.int32), sub.view(torch.int32))
+    assert torch.equal(full[:, idx[1:2]].contiguous().view(torch.int32), one.view(torch.int32))
+
+
+def test_vocabulary_shards_reproduce_the_unsharded_tiles():
+    n, vc, d = 200, 1000, 128
+    b = wl.lmhead_batch(n, vc, d, seed=5)
+    H, W, labels = to_dev_bf16(b.hidden), to_dev_bf16(b.weight), dev(b.labels)
+    full = bi.lmhead_tile_stats(H, W, labels)
+    # two shards split at a tile boundary: the same tiles, bit for bit
+    a = bi.lmhead_tile_stats(H, W[:512].contiguous(), labels, 0, vc)
+    c = bi.lmhead_tile_stats(H, W[512:].contiguous(), labels, 512, vc)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([a, c]).view(torch.int32), full.view(torch.int32))
+    # a split inside a tile: same combined result within tolerance
+    a = bi.lmhead_tile_stats(H, W[:300].contiguous(), labels, 0, vc)
+    c = bi.lmhead_tile_stats(H, W[300:].contiguous(), labels, 300, vc)
+    lp1, ent1, lse1 = bi.stats_combine(full, labels)
+    lp2, ent2, lse2 = bi.stats_combine(torch.cat([a, c]).contiguous(), labels)
+    torch.cuda.synchronize()
+    for x, y in ((lp1, lp2), (ent1, ent2), (lse1, lse2)):
+        assert_close(host(x), host(y), 1e-5, "sharded vs unsharded")
+
+
+def test_qwen3_vocab_sampled_tokens():
+    # the full Qwen3 vocabulary with a Qwen3-4B hidden size, sampled tokens
+    n, vc, d = 2048, wl.QWEN3_VOCAB, wl.LMHEAD_HIDDEN
+    b = wl.lmhead_batch(n, vc, d, seed=11, ignore_frac=0.02)
+    H, W, labels = to_dev_bf16(b.hidden), to_dev_bf16(b.weight), dev(b.labels)
+    lp, ent, lse = bi.lmhead_logprob(H, W, labels)
+    torch.cuda.synchronize()
+    rows = np.array(sorted({0, n - 1, *np.random.default_rng(1).choice(n, 24, replace=False)}))
+    z = orc.lmhead_logits(orc.decode(b.hidden[rows], "bf16"), orc.decode(b.weight, "bf16"))
+    olp, oent, olse = orc.forward(z, b.labels[rows])
+    assert_close(host(lp)[rows], olp, TOL, "logprob")
+    assert_close(host(ent)[rows], oent, TOL, "entropy")
+    assert_close(host(lse)[rows], olse, TOL, "lse")

@@ -137,6 +137,33 @@ def test_batch_invariance_sweep(fused):
     check_grads(core, np.arange(16), None, host(ref[4]), host(ref[3]))
 
 
+def test_chunk_and_multi_paths_are_batch_invariant():
+    # the 16 fixed rows: chunk statistics, combined outputs and multi-column
+    # logprobs must not depend on the batch either
+    V = wl.WORKLOADS[4].vocab
+    bounds = wl.chunk_bounds(V, wl.LARGE_CHUNKS)
+    per_n = {}
+    for n, cases in wl.invariance_batches(sizes=(1, 16, 512)):
+        outs = []
+        for case in cases:
+            logits = dev_logits(case.batch.logits, "bf16")
+            labels = dev(case.batch.labels)
+            st = torch.empty((len(bounds), case.batch.rows, 4), device="cuda")
+            for c, (a, e) in enumerate(bounds):
+                bi.vocab_chunk_stats(logits[:, a:e], labels, a, V, out=st[c])
+            clp, cent, clse = bi.stats_combine(st, labels)
+            ids = torch.stack([labels, torch.zeros_like(labels), labels.flip(0)], dim=1)
+            mlp, _, _ = bi.fwd_multi(logits, ids.contiguous())
+            pos = torch.from_numpy(case.positions).cuda()
+            outs.append((st[:, pos].reshape(-1), clp[pos], cent[pos], clse[pos], mlp[pos, :2].reshape(-1)))
+        torch.cuda.synchronize()
+        per_n[n] = [torch.cat([o[k] for o in outs]) for k in range(5)]
+    ref = per_n[1]
+    for n, got in per_n.items():
+        for k in range(5):
+            assert torch.equal(ref[k].view(torch.int32), got[k].view(torch.int32)), (n, k)
+
+
 def test_repeat_and_split_invariance():
     b = wl.draw(2, rows=np.arange(1024))
     logits, labels, w, lp, ent, lse, g, _ = _run_rows(b)

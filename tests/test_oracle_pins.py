@@ -575,3 +575,31 @@ def test_diff_stats_closed_cases():
                                             np.array([-0.0, 1.0], np.float32), [3, -100])
     assert (mean, amean, mx, ratio) == (0.0, 0.0, 0.0, 1.0)
     assert orc.diff_stats(a, b, [-100] * 4) == (0.0, 0.0, 0.0, 0.0)
+
+
+# ------------------------------------------------- lm_head projection + stats
+
+def test_lmhead_logits_brute_force_and_one_hot():
+    g = np.random.default_rng(21)
+    H = g.standard_normal((5, 7))
+    W = g.standard_normal((3, 7))
+    z = orc.lmhead_logits(H, W)
+    for n in range(5):
+        for v in range(3):
+            assert z[n, v] == pytest.approx(sum(H[n, k] * W[v, k] for k in range(7)), abs=1e-13)
+    # one-hot projection rows pick hidden coordinates (a transposed operand fails this)
+    W1 = np.zeros((7, 7))
+    W1[np.arange(7), (np.arange(7) * 3) % 7] = 1.0
+    np.testing.assert_array_equal(orc.lmhead_logits(H, W1), H[:, (np.arange(7) * 3) % 7])
+
+
+def test_lmhead_tile_stats_combine_to_the_full_row():
+    g = np.random.default_rng(22)
+    H = g.standard_normal((6, 16))
+    W = g.standard_normal((300, 16)) * 0.5
+    labels = np.array([0, 299, 128, 127, -100, 200])
+    st = orc.lmhead_tile_stats(H, W, labels, 0, 300, 128)
+    assert st.shape == (3, 6, 4)
+    lp, ent, lse = orc.combine(st, labels, 300)
+    flp, fent, flse = orc.forward(orc.lmhead_logits(H, W), labels)
+    np.testing.assert_allclose(np.stack([lp, ent, lse]), np.stack([flp, fent, flse]), atol=1e-12)

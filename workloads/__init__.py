@@ -256,3 +256,45 @@ def random_batch(rows: int, vocab: int, dtype: str, seed: int, sigma: float = 2.
     weights = (g.random(rows, dtype=np.float32) * np.float32(2.0)) if weighted else None
     logits = f32_to_bf16_bits(x) if dtype == "bf16" else x
     return Batch(logits, labels, weights, dtype, vocab)
+
+
+# ---------------------------------------------------------------------------
+# Hidden states and lm_head rows (bf16) whose products are N(0, sigma^2)-sized
+# logits: hidden ~ N(0, 1), weight ~ N(0, (sigma / sqrt(d))^2).  Qwen3-4B's
+# hidden size is 2,560 and its vocabulary 151,936.
+# ---------------------------------------------------------------------------
+
+LMHEAD_HIDDEN = 2560
+
+
+@dataclasses.dataclass
+class LmheadBatch:
+    hidden: np.ndarray      # uint16 bf16 bits [n, d]
+    weight: np.ndarray      # uint16 bf16 bits [V, d]
+    labels: np.ndarray      # int64 [n]
+
+
+def lmhead_batch(n: int, vocab: int, d: int, seed: int = DEFAULT_SEED, sigma: float = 2.0,
+                 ignore_frac: float = 0.0, threads: Optional[int] = None) -> LmheadBatch:
+    threads = default_threads() if threads is None else threads
+    hidden = np.empty((n, d), dtype=np.uint16)
+    weight = np.empty((vocab, d), dtype=np.uint16)
+    scale = np.float32(sigma / np.sqrt(d))
+
+    def rows(arr, kind, a, b, sc):
+        g = np.random.default_rng([seed, 600 + kind, a])
+        x = g.standard_normal((b - a, d), dtype=np.float32)
+        if sc is not None:
+            x *= sc
+        arr[a:b] = f32_to_bf16_bits(x)
+
+    blocks = [(hidden, 0, a, min(a + 1024, n), None) for a in range(0, n, 1024)] + \
+             [(weight, 1, a, min(a + 1024, vocab), scale) for a in range(0, vocab, 1024)]
+    with ThreadPoolExecutor(max(1, threads)) as ex:
+        list(ex.map(lambda t: rows(*t), blocks))
+    g = np.random.default_rng([seed, 700, n, vocab])
+    labels = g.integers(0, vocab, size=n).astype(np.int64)
+    k = int(round(ignore_frac * n))
+    if k:
+        labels[g.choice(n, size=k, replace=False)] = IGNORE_INDEX
+    return LmheadBatch(hidden, weight, labels)
