@@ -57,7 +57,9 @@ def algorithmic_bytes(vocab, e_in, e_grad, chunks):
 
 
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "large_32768x151936_bf16_hbm_traffic.md")
-KERNEL_SOURCE = os.path.join(ROOT, "entropy_bi_logprob_amd", "csrc", "bi_logprob.hip")
+# the sources of the row kernels (the counters below are only valid for them)
+KERNEL_SOURCES = [os.path.join(ROOT, "entropy_bi_logprob_amd", "csrc", f)
+                  for f in ("bi_common.h", "bi_logprob.hip")]
 
 
 def measured_traffic(kernel):
@@ -69,7 +71,10 @@ def measured_traffic(kernel):
     try:
         text = open(TRAFFIC_SUMMARY).read()
         block = json.loads(re.search(r"```json\n(.*?)\n```", text, re.S).group(1))
-        sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+        h = hashlib.sha256()
+        for f in KERNEL_SOURCES:
+            h.update(open(f, "rb").read())
+        sha = h.hexdigest()
     except (OSError, AttributeError, ValueError):
         return None
     if block.get("source_sha256") != sha or kernel not in block.get("per_launch", {}):

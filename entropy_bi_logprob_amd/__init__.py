@@ -23,6 +23,7 @@ import torch  # first: the library then binds to the HIP runtime torch has loade
 __all__ = [
     "IGNORE_INDEX", "BiError", "fwd", "bwd", "fwd_bwd", "policy_loss_fwd_bwd", "vocab_chunk_stats", "stats_combine",
     "row_geometry", "fwd_multi", "diff_stats", "lmhead_tile_stats", "lmhead_logprob",
+    "lmhead_tile_rows",
     "LogprobEntropy", "logprob_entropy", "lib",
     "library_path",
 ]
@@ -93,6 +94,8 @@ def lib() -> ctypes.CDLL:
     L.bi_lmhead_tile_stats.restype = i32
     L.bi_lmhead_tiles.argtypes = [i64]
     L.bi_lmhead_tiles.restype = i64
+    L.bi_lmhead_tile_rows.argtypes = []
+    L.bi_lmhead_tile_rows.restype = i64
     L.bi_stats_combine.argtypes = [vp, i64, i64, vp, i64, vp, vp, vp, vp]
     L.bi_row_geometry.argtypes = [i32, i64, ctypes.POINTER(i32), ctypes.POINTER(i32),
                                   ctypes.POINTER(i32)]
@@ -338,7 +341,8 @@ def lmhead_tile_stats(hidden: torch.Tensor, weight: torch.Tensor, labels: torch.
                       vocab_offset: int = 0, vocab: Optional[int] = None,
                       ignore_index: int = IGNORE_INDEX, *, out: Optional[torch.Tensor] = None,
                       status: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """[tiles, N, 4] statistics of hidden [N, d] @ weight[Vc, d]^T, by 128-row tiles.
+    """[tiles, N, 4] statistics of hidden [N, d] @ weight[Vc, d]^T, by tiles of
+    lmhead_tile_rows() lm_head rows.
 
     ``weight`` holds the lm_head rows of global vocabulary ids
     vocab_offset .. vocab_offset + Vc - 1; ``vocab`` is the global size
@@ -360,6 +364,11 @@ def lmhead_tile_stats(hidden: torch.Tensor, weight: torch.Tensor, labels: torch.
         _ptr(hidden), _ptr(weight), n, vc, d, ldh, ldw, vocab_offset, vocab, _ptr(labels),
         ignore_index, _ptr(out), _ptr(status), _stream(stream)))
     return out
+
+
+def lmhead_tile_rows() -> int:
+    """lm_head rows per statistics tile of lmhead_tile_stats."""
+    return int(lib().bi_lmhead_tile_rows())
 
 
 def lmhead_logprob(hidden: torch.Tensor, weight: torch.Tensor, labels: torch.Tensor,

@@ -14,7 +14,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "bi_logprob.hip")
+SOURCES = [os.path.join(PKG, "csrc", f) for f in ("bi_logprob.hip", "bi_lmhead.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libbi_logprob.so")
 ARCH = "gfx950"
@@ -40,7 +40,7 @@ def hipcc() -> str:
 def build(verbose: bool = False, extra_flags=(), out: str = LIB) -> str:
     """Compile the HIP library into ``out``; returns its path."""
     tmp = out + ".tmp"
-    cmd = [hipcc(), *FLAGS, *extra_flags, "-I", INCLUDE, "-o", tmp, SRC]
+    cmd = [hipcc(), *FLAGS, *extra_flags, "-I", INCLUDE, "-o", tmp, *SOURCES]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -1,0 +1,139 @@
+// bi_common.h - device helpers shared by the HIP translation units of
+// libbi_logprob (bi_logprob.hip: row kernels; bi_lmhead.hip: lm_head GEMM with
+// statistics), and the library's error state.  Internal: not installed, not
+// part of the C ABI.
+//
+// The lane accumulator keeps, in the log2 domain about a reference c (a
+// rounded -m*log2e for the running max m), S = sum 2^t and U = sum 2^t * t with
+// t = fma(z, log2e, c): the softmax denominator and the entropy-weighted sum
+// of "[RL] Avoid full-vocab gather for TP policy statistics" (torchtitan PR
+// #4685), Summary and Why, in a form that needs one FMA and one exp2 per logit.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <float.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "bi_logprob.h"
+
+namespace bi_internal {
+
+// Error text of the calling thread's last failed call (bi_last_error).
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int ok();
+bool aligned(const void* p, size_t a);
+int launched(const char* what);
+const char* last_error();
+
+}  // namespace bi_internal
+
+namespace {
+
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kLn2 = 0.693147180559945309417f;
+constexpr float kTFloor = -256.0f;   // 2^t == 0 in fp32 for every t below this
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// v_max3_f32 without the canonicalizing moves fmaxf would add around
+// non-arithmetic inputs (decoded bits).  NaN inputs still reach the sums.
+__device__ inline float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+__device__ inline float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ inline float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
+
+// log2-domain reference of a running max: c = -RN(m*log2e), kept finite for
+// m = -inf (an empty lane) so that no inf - inf arises.
+__device__ inline float ref_of(float m) { return fminf(-(m * kLog2e), FLT_MAX); }
+
+// --------------------------------------------------------- lane accumulator
+
+struct Acc {
+  float m;  // running max of the logits seen
+  float c;  // ref_of(m)
+  float S;  // sum of 2^t
+  float U;  // sum of 2^t * t   (log2 units, about c)
+};
+
+__device__ inline Acc acc_empty() { return Acc{-INFINITY, FLT_MAX, 0.0f, 0.0f}; }
+
+// Move an accumulator to the reference C (C <= a.c).  Exact no-op for C == a.c.
+__device__ inline void rebase(Acc& a, float C) {
+  const float d = fmaxf(C - a.c, kTFloor);
+  const float f = exp2_hw(d);
+  a.U = f * fmaf(d, a.S, a.U);
+  a.S = f * a.S;
+  a.c = C;
+}
+
+// max of K values through a fixed tree of v_max3 (K - 1 values removed per
+// two-operand step, so ceil((K - 1) / 2) instructions)
+template <int K>
+__device__ inline float max_reduce(const float* v) {
+  if constexpr (K == 1) {
+    return v[0];
+  } else if constexpr (K == 2) {
+    return max3(v[0], v[1], v[1]);
+  } else {
+    constexpr int Q = K / 3, R = K % 3;
+    float w[Q + R];
+#pragma unroll
+    for (int j = 0; j < Q; ++j) w[j] = max3(v[3 * j], v[3 * j + 1], v[3 * j + 2]);
+#pragma unroll
+    for (int r = 0; r < R; ++r) w[Q + r] = v[3 * Q + r];
+    return max_reduce<Q + R>(w);
+  }
+}
+
+template <int N>
+__device__ inline float tree_max(const float* z, float m) {
+  float v[N + 1];
+  v[0] = m;
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i + 1] = z[i];
+  return max_reduce<N + 1>(v);
+}
+
+template <int VEC>
+__device__ inline float tree_sum(const float* e) {
+  if constexpr (VEC == 8) {
+    return ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+  } else {
+    return (e[0] + e[1]) + (e[2] + e[3]);
+  }
+}
+
+// Accumulate NV vectors (NV*VEC decoded values, in lane order) into `a`.
+template <int VEC, int NV>
+__device__ inline void accumulate(Acc& a, const float* z) {
+  const float mx = tree_max<NV * VEC>(z, a.m);
+  const float c = ref_of(mx);
+  rebase(a, c);
+  a.m = mx;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    float e[VEC], tc[VEC];
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) {
+      const float t = fmaf(z[j * VEC + k], kLog2e, c);
+      e[k] = exp2_hw(t);              // 0 for z = -inf; NaN for NaN z
+      tc[k] = fmaxf(t, kTFloor);      // finite, so 0 * tc == 0 for masked columns
+    }
+    float u = e[0] * tc[0];
+#pragma unroll
+    for (int k = 1; k < VEC; ++k) u = fmaf(e[k], tc[k], u);
+    a.S += tree_sum<VEC>(e);
+    a.U += u;
+  }
+}
+
+}  // namespace

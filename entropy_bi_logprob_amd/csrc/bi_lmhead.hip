@@ -1,0 +1,467 @@
+// bi_lmhead.hip - the lm_head projection on the CDNA4 matrix cores, fused with
+// the per-token statistics of each vocabulary tile, so the [N, V] logits never
+// reach HBM.  C ABI: bi_lmhead_tile_stats, bi_lmhead_tiles, bi_lmhead_tile_rows
+// (include/bi_logprob.h); bi_stats_combine finishes.
+//
+// What is computed: the chunked lm_head of "ZeroSyncGRPOTrainer" (logits of a
+// vocabulary slice from the hidden states and the replicated projection, bf16
+// products accumulated in fp32), reduced at once to the shard-local statistics
+// of "[RL] Avoid full-vocab gather for TP policy statistics" (torchtitan PR
+// #4685), Why: local max, softmax denominator, target logit and the
+// entropy-weighted sum.  How it is computed is this file's own design:
+//
+//  * D[v][n] = sum_k W[v, k] H[n, k] with v_mfma_f32_32x32x16_bf16, A = lm_head
+//    rows, B = hidden rows.  Lane l of a 32 x 32 block holds token l % 32 and
+//    vocabulary rows 8*(r/4) + 4*(l/32) + r%4 of accumulator r, so a token's
+//    statistics need no shuffle inside a block.
+//  * A workgroup of 8 waves (2 per SIMD, one workgroup per CU) owns a
+//    256-vocab x 256-token tile: 2 (vocab) x 4 (tokens) waves, each a
+//    128 x 64 part (4 x 2 blocks, 128 accumulators).  The 256 x 256 tile keeps
+//    the operand bytes streamed from L2 per MFMA at their minimum for what the
+//    register file can hold.
+//  * K runs in stages of 64 through a 2-deep LDS ring (64 KB per stage) filled
+//    straight from global memory (global_load_lds_dwordx4, no register
+//    staging).  A stage is 4 MFMA K steps; each step's MFMAs are issued one by
+//    one with the next step's fragment reads between them.  Before the last
+//    step each wave waits for its own requests of stage s+1 and for its LDS
+//    reads of stage s, and the one barrier per stage both publishes stage s+1
+//    and frees stage s's buffer; the requests for stage s+2 are then spread
+//    between the last step's MFMAs, so the matrix pipe keeps running while
+//    they issue.
+//  * LDS rows are 128 bytes (8 chunks of 8 bf16).  Chunk c of row r is stored
+//    in slot c ^ g(r), g(r) = (r ^ ((r >> 3) & 3)) & 7, which puts the 8- and
+//    16-lane groups of every ds_read_b128 on distinct banks.  The shape knobs
+//    below also build 64-byte-row variants.
+//  * Rows past the end of W or H are read clamped to the last row (never out
+//    of bounds); their logits are masked to -inf / their tokens not written.
+//  * Each logit is the same MFMA sequence over K whatever n_tokens is, and the
+//    statistics of a tile are folded in a fixed order (the lane's 64 values,
+//    then the lane halves, then the two vocabulary waves), so the result of a
+//    token is batch-invariant bit for bit.
+//  * Tiles are visited XCD-aware: workgroup b runs on XCD b % 8, and each XCD
+//    takes a contiguous range of tiles in which 8 token tiles sweep the
+//    vocabulary tiles together, so concurrent tiles share W and H slices in
+//    that XCD's L2.
+
+#include "bi_common.h"
+
+namespace {
+
+using namespace bi_internal;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Tuning knobs (shape of the pipeline only; every choice computes the same
+// statistics tile of 256 vocabulary rows, bit for bit).
+#ifndef BI_LM_TILE_N
+#define BI_LM_TILE_N 256   // tokens per tile: 256 (one workgroup per CU) or 128
+#endif
+#ifndef BI_LM_RING
+#define BI_LM_RING 2       // LDS stages in the ring
+#endif
+#ifndef BI_LM_GROUP
+#define BI_LM_GROUP 8      // token tiles that sweep the vocabulary together
+#endif
+#ifndef BI_LM_BK
+#define BI_LM_BK 64        // K per LDS stage: 64 (128-byte row slices) or 32 (64-byte)
+#endif
+#ifndef BI_LM_WAVES
+#define BI_LM_WAVES 8      // waves per workgroup: 2 (vocab) x 4 (tokens) or 2 x 2
+#endif
+
+constexpr int kTV = 256;                  // vocab rows per tile (= per statistics tile)
+constexpr int kTN = BI_LM_TILE_N;         // tokens per tile
+constexpr int kWaves = BI_LM_WAVES;
+constexpr int kWT = kWaves / 2;           // token waves (vocab waves: 2)
+constexpr int kWV = kTV / 2;              // vocab rows per wave
+constexpr int kWN = kTN / kWT;            // tokens per wave
+constexpr int kXB = kWV / 32;             // 32-row MFMA blocks per wave: vocab
+constexpr int kYB = kWN / 32;             //                             tokens
+constexpr int kBK = BI_LM_BK;             // K per LDS stage
+constexpr int kKS = kBK / 16;             // MFMA K steps per stage
+constexpr int kChunks = kBK / 8;          // 16-byte chunks per row slice
+constexpr int kBlockRows = 1024 / (kBK * 2);   // rows per 1 KB fill block
+constexpr int kRing = BI_LM_RING;         // LDS stages in the ring
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRowBytes = kBK * 2;        // bytes per row per stage
+constexpr int kOpW = kTV * kRowBytes;     // W part of a stage
+constexpr int kStageBytes = (kTV + kTN) * kRowBytes;
+constexpr int kLoads = kStageBytes / (kThreads * 16);       // per lane per stage
+constexpr int kLoadsW = kOpW / (kThreads * 16);             // of which W
+constexpr int kGroup = BI_LM_GROUP;       // token tiles that sweep together
+
+static_assert(kStageBytes % (kThreads * 16) == 0 && kOpW % (kThreads * 16) == 0, "fill split");
+static_assert(kTN == 128 || kTN == 256, "tile shape");
+static_assert(kBK == 32 || kBK == 64, "stage depth");
+static_assert(kRing >= 2 && (kRing - 1) * kLoads < 64, "ring depth");
+static_assert(kRing * kStageBytes + 8192 <= 160 * 1024, "LDS size");
+static_assert(kWaves == 4 || kWaves == 8, "waves");
+static_assert(kWN % 32 == 0, "wave tile");
+static_assert(kXB * kYB >= kXB + kYB, "one fragment read per MFMA");
+// workgroups that fit one CU's 160 KB of LDS, hence waves per SIMD
+constexpr int kWGsPerCU = (160 * 1024) / (kRing * kStageBytes + kWT * kYB * 32 * 16);
+constexpr int kWavesPerEU = (kWGsPerCU > 2 ? 2 : kWGsPerCU) * kWaves / 4;
+
+struct LmArgs {
+  const uint16_t* hidden;   // [n_tok, ldh] bf16 bits
+  const uint16_t* weight;   // [n_voc, ldw] bf16 bits
+  int64_t n_tok, n_voc, d, ldh, ldw;
+  int64_t vocab_offset, vocab;
+  const int64_t* labels;
+  int64_t ignore_index;
+  bi_stats* stats;          // [tiles_v][n_tok]
+  int32_t* status_flag;
+  int64_t tiles_v, tiles_n;
+};
+
+// Tile (tv, tn) of workgroup b; false for the padding workgroups of the grid.
+__device__ inline bool lm_tile_of(const LmArgs& p, int64_t b, int64_t* tv, int64_t* tn) {
+  const int64_t total = p.tiles_v * p.tiles_n;
+  const int64_t per_xcd = (total + 7) / 8;
+  const int64_t t = (b % 8) * per_xcd + b / 8;
+  if (t >= total) return false;
+  const int64_t group = t / (kGroup * p.tiles_v), r = t % (kGroup * p.tiles_v);
+  const int64_t rows_in_group = min(int64_t(kGroup), p.tiles_n - group * kGroup);
+  *tn = group * kGroup + r % rows_in_group;
+  *tv = r / rows_in_group;
+  return true;
+}
+
+// Slot of a row's 16-byte chunks in LDS: chunk c of row r sits in slot
+// c ^ lm_swz(r).  It depends only on r mod 32 (so it is the same for every
+// 32-row MFMA block) and makes the 8- and 16-lane groups of a ds_read_b128
+// (rows r0 .. r0+7 or r0+15, one chunk each) hit distinct bank groups.
+__device__ inline int lm_swz(int r) {
+  if constexpr (kChunks == 4) return ((r >> 1) ^ (r >> 2)) & 3;   // 64-byte rows
+  else return (r ^ ((r >> 3) & 3)) & 7;                          // 128-byte rows
+}
+
+// s_waitcnt on the vector-memory and LDS counters (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt 6:4 left at its maximum, lgkmcnt 11:8)
+template <int VM, int LGKM>
+__device__ inline void wait_counts() {
+  static_assert(VM >= 0 && VM < 64 && LGKM >= 0 && LGKM < 16, "waitcnt range");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (LGKM << 8));
+}
+
+// Workgroup barrier that orders LDS traffic in the compiler but adds no wait
+// of its own (the waits are explicit).
+__device__ inline void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// This lane's part of the direct-to-LDS fill: kLoads requests per stage,
+// each 16 bytes of global memory into 16 bytes of a 1 KB block that the wave
+// writes contiguously (lane order).  Block q of a stage holds kBlockRows
+// operand rows, of W for the first kLoadsW*4 blocks, then of H.
+struct LmFill {
+  const char* src[kLoads];   // global address of this lane's chunk at k = 0
+  uint32_t lds[kLoads];      // wave-uniform LDS byte offset within a stage
+};
+
+__device__ inline LmFill lm_fill_setup(const LmArgs& p, int64_t v0, int64_t n0, int wave,
+                                       int lane) {
+  LmFill f;
+  const int rb = lane / kChunks, slot = lane % kChunks;
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) {
+    const int q = wave + kWaves * i;              // all blocks over the waves
+    const bool is_w = i < kLoadsW;                // a W block exactly when i < kLoadsW
+    const int r = kBlockRows * (is_w ? q : q - kLoadsW * kWaves) + rb;   // operand row
+    const int c = slot ^ lm_swz(r);               // global chunk stored in this slot
+    const int64_t row = is_w ? min(v0 + r, p.n_voc - 1) : min(n0 + r, p.n_tok - 1);
+    const uint16_t* base = is_w ? p.weight + row * p.ldw : p.hidden + row * p.ldh;
+    f.src[i] = reinterpret_cast<const char*>(base + 8 * c);
+    f.lds[i] = uint32_t(q) * 1024u;
+  }
+  return f;
+}
+
+// LDS byte address of a pointer into shared memory.
+__device__ inline uint32_t lds_addr(const char* p) {
+  return uint32_t(reinterpret_cast<uintptr_t>((const lds_void*)p));
+}
+
+// Request stage `stage` into the ring buffer `dst`.  Written as inline
+// assembly so that the compiler does not track these LDS writes: it would
+// otherwise wait for every request in flight before any LDS read.  The waits
+// are explicit instead (wait_counts before each barrier); the compiler's own
+// vmcnt waits stay correct, since extra requests only make them stricter.
+// The LDS-DMA load reads M0, which the compiler writes just before the asm
+// with a scalar instruction: one wait state (s_nop 0) must separate the two.
+__device__ inline void lm_fill1(const LmFill& f, uint32_t base, int stage, int i) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(f.src[i] + stage * kRowBytes), "{m0}"(base + f.lds[i])
+               : "memory");
+}
+
+__device__ inline void lm_fill(const LmFill& f, const char* dst, int stage) {
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) lm_fill1(f, lds_addr(dst), stage, i);
+}
+
+struct LmFrag {
+  bf16x8 a[kXB], b[kYB];
+};
+
+// Operand fragment j of one K step of the stage held in the ring buffer s,
+// in the order the step's MFMAs first use them (A0, B0 .. B(kYB-1), A1 ..).
+__device__ inline void lm_read1(LmFrag& fr, const char* s, uint32_t off_w, uint32_t off_h,
+                                int j) {
+  if (j >= 1 && j <= kYB) {
+    fr.b[j - 1] = *reinterpret_cast<const bf16x8*>(s + off_h + (j - 1) * 32 * kRowBytes);
+  } else {
+    const int x = j == 0 ? 0 : j - kYB;
+    fr.a[x] = *reinterpret_cast<const bf16x8*>(s + off_w + x * 32 * kRowBytes);
+  }
+}
+
+__device__ inline void lm_read(LmFrag& fr, const char* s, uint32_t off_w, uint32_t off_h) {
+#pragma unroll
+  for (int j = 0; j < kXB + kYB; ++j) lm_read1(fr, s, off_w, off_h, j);
+}
+
+constexpr int kMfmas = kXB * kYB;                      // MFMAs per wave per K step
+constexpr int kFillsPerMfma = (kLoads + kMfmas - 1) / kMfmas;
+
+// The MFMAs of one K step (fragments `cur`), each followed by `extra(m)`: the
+// reads and requests that the step overlaps are issued one by one between
+// the MFMAs, so the matrix pipe never waits for a burst of them.  The
+// scheduling barriers keep exactly this order.
+template <typename Extra>
+__device__ inline void lm_mma_with(const LmFrag& cur, f32x16 (&acc)[kXB][kYB], Extra&& extra) {
+#pragma unroll
+  for (int m = 0; m < kMfmas; ++m) {
+    const int x = m / kYB, y = m % kYB;
+    acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.a[x], cur.b[y], acc[x][y], 0, 0, 0);
+    extra(m);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// (m, c, S, U, t) of one token: a (+) b with a taken first
+__device__ inline void lm_merge(Acc& a, float& ta, const Acc& b, float tb) {
+  const float M = fmaxf(a.m, b.m);
+  const float C = ref_of(M);
+  Acc x = a, y = b;
+  rebase(x, C);
+  rebase(y, C);
+  a.m = M;
+  a.c = C;
+  a.S = x.S + y.S;
+  a.U = x.U + y.U;
+  ta = ta + tb;
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEU, kWavesPerEU)))
+void lmhead_stats_kernel(LmArgs p) {
+  __shared__ __attribute__((aligned(1024))) char ring[kRing * kStageBytes];
+  __shared__ float red[kWT][kYB][32][4];
+  int64_t tv, tn;
+  if (!lm_tile_of(p, blockIdx.x, &tv, &tn)) return;   // whole workgroup exits together
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wv = wave & 1, wt = wave >> 1;
+  const int64_t v0 = tv * kTV, n0 = tn * kTN;
+  const int lr = lane & 31, half = lane >> 5;
+
+  // the labels of this lane's tokens, fetched early (used by the epilogue)
+  int64_t lab[kYB];
+#pragma unroll
+  for (int y = 0; y < kYB; ++y) {
+    const int64_t j = n0 + kWN * wt + 32 * y + lr;
+    lab[y] = j < p.n_tok ? p.labels[j] : p.ignore_index;
+  }
+
+  const LmFill fill = lm_fill_setup(p, v0, n0, wave, lane);
+  const int ns = int(p.d / kBK);
+
+  // this lane's fragment offsets within a stage, for each K step
+  uint32_t off_w[kKS], off_h[kKS];
+#pragma unroll
+  for (int kk = 0; kk < kKS; ++kk) {
+    const uint32_t in_row = uint32_t(lr * kRowBytes + 16 * ((2 * kk + half) ^ lm_swz(lr)));
+    off_w[kk] = uint32_t(kWV * wv * kRowBytes) + in_row;
+    off_h[kk] = uint32_t(kOpW + kWN * wt * kRowBytes) + in_row;
+  }
+
+  f32x16 acc[kXB][kYB];
+#pragma unroll
+  for (int x = 0; x < kXB; ++x)
+#pragma unroll
+    for (int y = 0; y < kYB; ++y)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[x][y][r] = 0.0f;
+
+  // prologue: stages 0 .. kRing-1 requested, stage 0 landed and visible.  Requests
+  // past the last stage re-read the last stage into a buffer nobody reads
+  // again, so every stage has the same kLoads requests per lane in flight.
+#pragma unroll
+  for (int b = 0; b < kRing; ++b) lm_fill(fill, ring + b * kStageBytes, min(b, ns - 1));
+  wait_counts<(kRing - 1) * kLoads, 15>();
+  lds_barrier();
+  LmFrag fr[2];
+  lm_read(fr[0], ring, off_w[0], off_h[0]);
+
+  // Stage s from ring buffer `cur`, K step kk's fragments in fr[kk & 1]: the
+  // next step's fragments are read while this step's MFMAs run.  Before the
+  // last step's MFMAs: stage s+1 must have landed (this wave's requests; the
+  // barrier covers the other waves') and this wave's reads of stage s must be
+  // done; after the barrier stage s+1 is visible and stage s's buffer is free
+  // for stage s+kRing, whose requests are spread over the last step.
+  int cur = 0;
+  for (int s = 0; s < ns; ++s) {
+    const int nxt = cur == kRing - 1 ? 0 : cur + 1;
+    const char* cbuf = ring + cur * kStageBytes;
+#pragma unroll
+    for (int kk = 0; kk < kKS; ++kk) {
+      LmFrag& now = fr[kk & 1];
+      LmFrag& next = fr[(kk + 1) & 1];
+      if (kk + 1 < kKS) {
+        lm_mma_with(now, acc, [&](int m) {
+          if (m < kXB + kYB) lm_read1(next, cbuf, off_w[kk + 1], off_h[kk + 1], m);
+        });
+      } else {
+        wait_counts<(kRing - 2) * kLoads, 0>();
+        lds_barrier();
+        const uint32_t fbase = lds_addr(cbuf);
+        const int fstage = min(s + kRing, ns - 1);
+        const char* nbuf = ring + nxt * kStageBytes;
+        lm_mma_with(now, acc, [&](int m) {
+#pragma unroll
+          for (int u = 0; u < kFillsPerMfma; ++u)
+            if (m * kFillsPerMfma + u < kLoads) lm_fill1(fill, fbase, fstage, m * kFillsPerMfma + u);
+          if (m < kXB + kYB) lm_read1(next, nbuf, off_w[0], off_h[0], m);
+        });
+      }
+    }
+    cur = nxt;
+  }
+  wait_counts<0, 15>();   // no request may still be writing LDS when the workgroup ends
+
+  // epilogue: statistics of each token over this tile's 256 vocabulary rows
+  const bool full = v0 + kTV <= p.n_voc;   // uniform: no row of the tile is masked
+  const int64_t wrow0 = v0 + kWV * wv;     // first vocabulary row of this wave
+  float tl[kYB];
+  Acc lo[kYB];
+#pragma unroll
+  for (int y = 0; y < kYB; ++y) {
+    float z[16 * kXB];
+#pragma unroll
+    for (int x = 0; x < kXB; ++x)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t i = wrow0 + 32 * x + 8 * (r >> 2) + 4 * half + (r & 3);
+        z[16 * x + r] = (full || i < p.n_voc) ? acc[x][y][r] : -INFINITY;
+      }
+    Acc a = acc_empty();
+    accumulate<8, 2 * kXB>(a, z);
+    // the label's logit, held by exactly one lane of one vocabulary wave (if
+    // here); the select chain runs only when some lane of the wave needs it
+    float t = 0.0f;
+    const bool bad = lab[y] != p.ignore_index && (lab[y] < 0 || lab[y] >= p.vocab);
+    const int64_t yl = lab[y] - p.vocab_offset - wrow0;   // row within this wave's 128
+    const bool mine = !bad && lab[y] != p.ignore_index && lab[y] - p.vocab_offset < p.n_voc &&
+                      yl >= 0 && yl < kWV && half == ((yl >> 2) & 1);
+    if (__builtin_amdgcn_ballot_w64(mine)) {
+      const int q = int(yl >> 5) * 16 + int((yl & 31) >> 3) * 4 + int(yl & 3);
+#pragma unroll
+      for (int k = 0; k < 16 * kXB; ++k)
+        if (mine && q == k) t = z[k];
+    }
+    // lane halves (same token, other rows), lower half first
+    Acc o;
+    o.m = __shfl_xor(a.m, 32);
+    o.c = __shfl_xor(a.c, 32);
+    o.S = __shfl_xor(a.S, 32);
+    o.U = __shfl_xor(a.U, 32);
+    const float ot = __shfl_xor(t, 32);
+    Acc l = half ? o : a, h = half ? a : o;
+    float tlo = half ? ot : t, thi = half ? t : ot;
+    lm_merge(l, tlo, h, thi);
+    lo[y] = l;
+    tl[y] = tlo;
+    if (wv == 1 && half == 0) {
+      red[wt][y][lr][0] = l.m;
+      red[wt][y][lr][1] = l.S;
+      red[wt][y][lr][2] = l.U;
+      red[wt][y][lr][3] = tlo;
+    }
+  }
+  __syncthreads();
+  if (wv == 0 && half == 0) {
+#pragma unroll
+    for (int y = 0; y < kYB; ++y) {
+      const int64_t j = n0 + kWN * wt + 32 * y + lr;
+      Acc b;
+      b.m = red[wt][y][lr][0];
+      b.c = ref_of(b.m);
+      b.S = red[wt][y][lr][1];
+      b.U = red[wt][y][lr][2];
+      Acc a = lo[y];
+      float t = tl[y];
+      lm_merge(a, t, b, red[wt][y][lr][3]);
+      if (j < p.n_tok) {
+        const bool bad = lab[y] != p.ignore_index && (lab[y] < 0 || lab[y] >= p.vocab);
+        const float d = fmaf(a.m, kLog2e, a.c);
+        const float f = exp2_hw(-d);
+        bi_stats out;
+        out.max = a.m;
+        out.sumexp = a.S == 0.0f ? 0.0f : a.S * f;
+        out.sumexp_logit = a.S == 0.0f ? 0.0f : kLn2 * (fmaf(-d, a.S, a.U) * f);
+        out.target = bad ? NAN : t;
+        p.stats[tv * p.n_tok + j] = out;
+        if (bad && p.status_flag) atomicOr(p.status_flag, BI_FLAG_BAD_LABEL);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t bi_lmhead_tile_rows(void) { return kTV; }
+
+int64_t bi_lmhead_tiles(int64_t n_vocab_rows) {
+  return n_vocab_rows <= 0 ? 0 : (n_vocab_rows + kTV - 1) / kTV;
+}
+
+int bi_lmhead_tile_stats(const void* hidden, const void* weight, int64_t n_tokens,
+                         int64_t n_vocab_rows, int64_t d, int64_t hidden_stride,
+                         int64_t weight_stride, int64_t vocab_offset, int64_t vocab,
+                         const int64_t* labels, int64_t ignore_index, bi_stats* stats,
+                         int32_t* status_flag, bi_stream_t stream) {
+  const char* fn = "bi_lmhead_tile_stats";
+  if (n_tokens < 0 || n_vocab_rows < 0)
+    return fail(BI_ERR_SHAPE, "%s: negative size", fn);
+  if (d < kBK || d % kBK != 0 || d > (int64_t(1) << 24))
+    return fail(BI_ERR_SHAPE, "%s: d = %lld must be a positive multiple of %d (at most 2^24)",
+                fn, (long long)d, kBK);
+  if (hidden_stride < d || weight_stride < d || hidden_stride % 8 || weight_stride % 8)
+    return fail(BI_ERR_SHAPE, "%s: strides must be >= d and multiples of 8 elements", fn);
+  if (vocab < 1 || vocab_offset < 0 || vocab_offset + n_vocab_rows > vocab)
+    return fail(BI_ERR_SHAPE, "%s: rows [%lld, %lld) outside the vocabulary [0, %lld)", fn,
+                (long long)vocab_offset, (long long)(vocab_offset + n_vocab_rows),
+                (long long)vocab);
+  if (n_tokens == 0 || n_vocab_rows == 0) return ok();
+  if (!hidden || !weight || !labels || !stats)
+    return fail(BI_ERR_NULL, "%s: hidden, weight, labels and stats are required", fn);
+  if (!aligned(hidden, 16) || !aligned(weight, 16) || !aligned(labels, 8) ||
+      !aligned(stats, 16) || !aligned(status_flag, 4))
+    return fail(BI_ERR_ALIGN, "%s: hidden and weight need 16-byte alignment", fn);
+  LmArgs a{static_cast<const uint16_t*>(hidden), static_cast<const uint16_t*>(weight),
+           n_tokens, n_vocab_rows, d, hidden_stride, weight_stride, vocab_offset, vocab,
+           labels, ignore_index, stats, status_flag, bi_lmhead_tiles(n_vocab_rows),
+           (n_tokens + kTN - 1) / kTN};
+  const int64_t total = a.tiles_v * a.tiles_n;
+  const int64_t blocks = 8 * ((total + 7) / 8);
+  if (blocks > 0x7fffffff) return fail(BI_ERR_SHAPE, "%s: too many tiles", fn);
+  hipLaunchKernelGGL(lmhead_stats_kernel, dim3(unsigned(blocks)), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), a);
+  return launched(fn);
+}
+
+}  // extern "C"

@@ -33,22 +33,13 @@
 //    dword-aligned dwordx4); bf16 rows on a 2-byte boundary take an element
 //    path with the same column map and arithmetic.
 
-#include <hip/hip_runtime.h>
 
-#include <float.h>
-#include <math.h>
-#include <stdarg.h>
-#include <stdint.h>
-#include <stdio.h>
-#include <string.h>
-
-#include "bi_logprob.h"
+#include "bi_common.h"
 
 namespace {
 
-constexpr float kLog2e = 1.44269504088896340736f;
-constexpr float kLn2 = 0.693147180559945309417f;
-constexpr float kTFloor = -256.0f;   // 2^t == 0 in fp32 for every t below this
+using namespace bi_internal;
+
 constexpr int kMaxThreads = 1024;
 constexpr int kMaxWaves = kMaxThreads / 64;
 constexpr int64_t kMaxWidth = int64_t(1) << 29;
@@ -61,7 +52,6 @@ constexpr int64_t kMaxWidth = int64_t(1) << 29;
 #endif
 constexpr int kGroupElems = BI_GROUP_ELEMS;   // elements per lane per rescale
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 
 struct Geometry {
@@ -166,101 +156,6 @@ __device__ inline u32x4 fetch(const RowSrc& s, uint32_t k) {
   }
 }
 
-// v_max3_f32 without the canonicalizing moves fmaxf would add around
-// non-arithmetic inputs (decoded bits).  NaN inputs still reach the sums.
-__device__ inline float max3(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
-
-__device__ inline float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
-__device__ inline float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
-
-// log2-domain reference of a running max: c = -RN(m*log2e), kept finite for
-// m = -inf (an empty lane) so that no inf - inf arises.
-__device__ inline float ref_of(float m) { return fminf(-(m * kLog2e), FLT_MAX); }
-
-// --------------------------------------------------------- lane accumulator
-
-struct Acc {
-  float m;  // running max of the logits seen
-  float c;  // ref_of(m)
-  float S;  // sum of 2^t
-  float U;  // sum of 2^t * t   (log2 units, about c)
-};
-
-__device__ inline Acc acc_empty() { return Acc{-INFINITY, FLT_MAX, 0.0f, 0.0f}; }
-
-// Move an accumulator to the reference C (C <= a.c).  Exact no-op for C == a.c.
-__device__ inline void rebase(Acc& a, float C) {
-  const float d = fmaxf(C - a.c, kTFloor);
-  const float f = exp2_hw(d);
-  a.U = f * fmaf(d, a.S, a.U);
-  a.S = f * a.S;
-  a.c = C;
-}
-
-// max of K values through a fixed tree of v_max3 (K - 1 values removed per
-// two-operand step, so ceil((K - 1) / 2) instructions)
-template <int K>
-__device__ inline float max_reduce(const float* v) {
-  if constexpr (K == 1) {
-    return v[0];
-  } else if constexpr (K == 2) {
-    return max3(v[0], v[1], v[1]);
-  } else {
-    constexpr int Q = K / 3, R = K % 3;
-    float w[Q + R];
-#pragma unroll
-    for (int j = 0; j < Q; ++j) w[j] = max3(v[3 * j], v[3 * j + 1], v[3 * j + 2]);
-#pragma unroll
-    for (int r = 0; r < R; ++r) w[Q + r] = v[3 * Q + r];
-    return max_reduce<Q + R>(w);
-  }
-}
-
-template <int N>
-__device__ inline float tree_max(const float* z, float m) {
-  float v[N + 1];
-  v[0] = m;
-#pragma unroll
-  for (int i = 0; i < N; ++i) v[i + 1] = z[i];
-  return max_reduce<N + 1>(v);
-}
-
-template <int VEC>
-__device__ inline float tree_sum(const float* e) {
-  if constexpr (VEC == 8) {
-    return ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
-  } else {
-    return (e[0] + e[1]) + (e[2] + e[3]);
-  }
-}
-
-// Accumulate NV vectors (NV*VEC decoded values, in lane order) into `a`.
-template <int VEC, int NV>
-__device__ inline void accumulate(Acc& a, const float* z) {
-  const float mx = tree_max<NV * VEC>(z, a.m);
-  const float c = ref_of(mx);
-  rebase(a, c);
-  a.m = mx;
-#pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    float e[VEC], tc[VEC];
-#pragma unroll
-    for (int k = 0; k < VEC; ++k) {
-      const float t = fmaf(z[j * VEC + k], kLog2e, c);
-      e[k] = exp2_hw(t);              // 0 for z = -inf; NaN for NaN z
-      tc[k] = fmaxf(t, kTFloor);      // finite, so 0 * tc == 0 for masked columns
-    }
-    float u = e[0] * tc[0];
-#pragma unroll
-    for (int k = 1; k < VEC; ++k) u = fmaf(e[k], tc[k], u);
-    a.S += tree_sum<VEC>(e);
-    a.U += u;
-  }
-}
 
 template <int DT, int G, bool VLOAD, int POL = kNonTemporal>
 __device__ inline void load_group(u32x4* buf, const RowSrc& src, uint32_t g) {
@@ -949,248 +844,45 @@ __global__ __launch_bounds__(kDiffThreads) void diff_stats_kernel(
   }
 }
 
-// ------------------------------------------------ lm_head GEMM + statistics
-//
-// The logits of a vocabulary chunk computed on the matrix cores from the
-// hidden states and the lm_head rows, and reduced at once to per-token
-// statistics, so the [N, V] logits never reach HBM (the chunked lm_head of
-// "ZeroSyncGRPOTrainer", with the shard-local statistics of PR #4685 Why).
-//
-// MFMA v_mfma_f32_32x32x16_bf16 with A = lm_head rows W[v, k] and B = hidden
-// rows H[n, k]: D[v][n] = sum_k W[v, k] H[n, k], so each lane holds one
-// token's column and the statistics of a token need no shuffles within a
-// 32 x 32 block (lane l: token l % 32, vocab rows 8*(r/4) + 4*(l/32) + r%4 of
-// accumulator r).  A workgroup of 4 waves owns a 128-vocab x 128-token tile
-// (each wave 64 x 64, i.e. 2 x 2 blocks) and runs over all of K in LDS stages
-// of 64, double-buffered.  Every logit is the same fixed sequence of MFMAs
-// over K whatever N is, so the statistics are batch-invariant.  The epilogue
-// folds the tile's 128 logits of each token into one bi_stats (fixed order:
-// the lane's 32 values, then the lane halves, then the two vocab waves),
-// written as "chunk" tv of the token; bi_stats_combine then reduces the
-// tiles in ascending order.
+// Eight lanes per row: lane q takes chunks q, q+8, q+16, ... in ascending
+// order, then the eight partial sums are added by a fixed xor butterfly
+// (1, 2, 4), which leaves the same bits in every lane.  The order depends on
+// n_chunks only (batch-invariant).  Natural units throughout.
+constexpr int kCombineLanes = 8;
+constexpr int kCombineThreads = 256;
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+__device__ inline float xor_max(float v, int m) { return fmaxf(v, __shfl_xor(v, m, 64)); }
+__device__ inline float xor_add(float v, int m) { return v + __shfl_xor(v, m, 64); }
 
-constexpr int kLmTile = 128;        // vocab rows and tokens per workgroup tile
-constexpr int kLmBK = 64;           // K per LDS stage
-constexpr int kLmRow = kLmBK + 8;   // LDS row pitch in bf16: 144 bytes spreads the banks
-constexpr int kLmThreads = 256;     // 4 waves: 2 (vocab) x 2 (tokens)
-
-struct LmArgs {
-  const uint16_t* hidden;   // [n_tok, ldh] bf16 bits
-  const uint16_t* weight;   // [n_voc, ldw] bf16 bits
-  int64_t n_tok, n_voc, d, ldh, ldw;
-  int64_t vocab_offset, vocab;
-  const int64_t* labels;
-  int64_t ignore_index;
-  bi_stats* stats;          // [tiles_v][n_tok]
-  int32_t* status_flag;
-  int64_t tiles_v, tiles_n;
-};
-
-// Tile of block b.  Workgroups go to the 8 XCDs round-robin; each XCD gets a
-// contiguous run of tiles, in which groups of 8 token tiles sweep the
-// vocabulary tiles together, so the W and H slices in flight are shared
-// through that XCD's L2.
-__device__ inline bool lm_tile_of(const LmArgs& p, int64_t b, int64_t* tv, int64_t* tn) {
-  const int64_t total = p.tiles_v * p.tiles_n;
-  const int64_t per_xcd = (total + 7) / 8;
-  const int64_t t = (b % 8) * per_xcd + b / 8;
-  if (t >= total) return false;
-  const int64_t group = t / (8 * p.tiles_v), r = t % (8 * p.tiles_v);
-  const int64_t rows_in_group = min(int64_t(8), p.tiles_n - group * 8);
-  *tn = group * 8 + r % rows_in_group;
-  *tv = r / rows_in_group;
-  return *tv < p.tiles_v;
-}
-
-struct LmStage {
-  u32x4 w[4], h[4];
-};
-
-__device__ inline void lm_load(const LmArgs& p, int64_t v0, int64_t n0, int64_t k0, int tid,
-                               LmStage& st) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int q = tid + kLmThreads * i;   // 0..1023: row q/8, 16-byte column q%8
-    const int row = q >> 3, kv = q & 7;
-    const int64_t v = v0 + row, n = n0 + row;
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    st.w[i] = v < p.n_voc
-                  ? *reinterpret_cast<const u32x4*>(p.weight + v * p.ldw + k0 + 8 * kv)
-                  : zero;
-    st.h[i] = n < p.n_tok
-                  ? *reinterpret_cast<const u32x4*>(p.hidden + n * p.ldh + k0 + 8 * kv)
-                  : zero;
-  }
-}
-
-__device__ inline void lm_store(uint16_t* sW, uint16_t* sH, int tid, const LmStage& st) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int q = tid + kLmThreads * i;
-    const int row = q >> 3, kv = q & 7;
-    *reinterpret_cast<u32x4*>(sW + row * kLmRow + 8 * kv) = st.w[i];
-    *reinterpret_cast<u32x4*>(sH + row * kLmRow + 8 * kv) = st.h[i];
-  }
-}
-
-__device__ inline void lm_mma_stage(const uint16_t* sW, const uint16_t* sH, int wv, int wt,
-                                    int lane, f32x16 (&acc)[2][2]) {
-  const int lr = lane & 31, lk = 8 * (lane >> 5);
-#pragma unroll
-  for (int kk = 0; kk < kLmBK / 16; ++kk) {
-    bf16x8 a[2], b[2];
-#pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      a[x] = *reinterpret_cast<const bf16x8*>(sW + (64 * wv + 32 * x + lr) * kLmRow + 16 * kk + lk);
-      b[x] = *reinterpret_cast<const bf16x8*>(sH + (64 * wt + 32 * x + lr) * kLmRow + 16 * kk + lk);
-    }
-#pragma unroll
-    for (int x = 0; x < 2; ++x)
-#pragma unroll
-      for (int y = 0; y < 2; ++y)
-        acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[x], b[y], acc[x][y], 0, 0, 0);
-  }
-}
-
-// (m, c, S, U, t) of one token: a (+) b with a taken first
-__device__ inline void lm_merge(Acc& a, float& ta, const Acc& b, float tb) {
-  const float M = fmaxf(a.m, b.m);
-  const float C = ref_of(M);
-  Acc x = a, y = b;
-  rebase(x, C);
-  rebase(y, C);
-  a.m = M;
-  a.c = C;
-  a.S = x.S + y.S;
-  a.U = x.U + y.U;
-  ta = ta + tb;
-}
-
-__global__ __launch_bounds__(kLmThreads) void lmhead_stats_kernel(LmArgs p) {
-  __shared__ __attribute__((aligned(16))) uint16_t sW[2][kLmTile * kLmRow];
-  __shared__ __attribute__((aligned(16))) uint16_t sH[2][kLmTile * kLmRow];
-  __shared__ float red[2][2][32][4];
-  int64_t tv, tn;
-  if (!lm_tile_of(p, blockIdx.x, &tv, &tn)) return;   // whole workgroup exits together
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wv = wave & 1, wt = wave >> 1;
-  const int64_t v0 = tv * kLmTile, n0 = tn * kLmTile;
-
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int x = 0; x < 2; ++x)
-#pragma unroll
-    for (int y = 0; y < 2; ++y)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[x][y][r] = 0.0f;
-
-  const int64_t stages = p.d / kLmBK;
-  LmStage st;
-  lm_load(p, v0, n0, 0, tid, st);
-  lm_store(sW[0], sH[0], tid, st);
-  __syncthreads();
-  for (int64_t s = 0; s + 1 < stages; ++s) {
-    lm_load(p, v0, n0, (s + 1) * kLmBK, tid, st);
-    lm_mma_stage(sW[s & 1], sH[s & 1], wv, wt, lane, acc);
-    lm_store(sW[(s + 1) & 1], sH[(s + 1) & 1], tid, st);
-    __syncthreads();
-  }
-  lm_mma_stage(sW[(stages - 1) & 1], sH[(stages - 1) & 1], wv, wt, lane, acc);
-
-  // epilogue: statistics of each token over this tile's 128 vocabulary rows
-#pragma unroll
-  for (int y = 0; y < 2; ++y) {
-    const int64_t j = n0 + 64 * wt + 32 * y + (lane & 31);
-    float z[32];
-#pragma unroll
-    for (int x = 0; x < 2; ++x)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t i = v0 + 64 * wv + 32 * x + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        z[16 * x + r] = i < p.n_voc ? acc[x][y][r] : -INFINITY;
-      }
-    Acc a = acc_empty();
-    accumulate<8, 4>(a, z);
-    // the label's logit, held by exactly one lane of one vocab wave (if here)
-    float t = 0.0f;
-    const int64_t lab = j < p.n_tok ? p.labels[j] : p.ignore_index;
-    const bool bad = lab != p.ignore_index && (lab < 0 || lab >= p.vocab);
-    const int64_t local = lab - p.vocab_offset;               // row within these lm_head rows
-    const int64_t yl = local - v0 - 64 * wv;                  // row within this wave's 64
-    if (!bad && lab != p.ignore_index && local < p.n_voc && yl >= 0 && yl < 64) {
-      const int x = int(yl >> 5), rr = int(yl & 31);
-      if ((lane >> 5) == ((rr >> 2) & 1)) {
-        const int r = (rr >> 3) * 4 + (rr & 3);
-#pragma unroll
-        for (int q = 0; q < 32; ++q)
-          if (q == 16 * x + r) t = z[q];
-      }
-    }
-    // lane halves (same token, other rows), lower half first
-    Acc o;
-    o.m = __shfl_xor(a.m, 32);
-    o.c = __shfl_xor(a.c, 32);
-    o.S = __shfl_xor(a.S, 32);
-    o.U = __shfl_xor(a.U, 32);
-    const float ot = __shfl_xor(t, 32);
-    Acc lo = (lane < 32) ? a : o, hi = (lane < 32) ? o : a;
-    float tlo = (lane < 32) ? t : ot, thi = (lane < 32) ? ot : t;
-    lm_merge(lo, tlo, hi, thi);
-    if (wv == 1 && lane < 32) {
-      red[wt][y][lane][0] = lo.m;
-      red[wt][y][lane][1] = lo.S;
-      red[wt][y][lane][2] = lo.U;
-      red[wt][y][lane][3] = tlo;
-    }
-    __syncthreads();
-    if (wv == 0 && lane < 32) {
-      Acc b;
-      b.m = red[wt][y][lane][0];
-      b.c = ref_of(b.m);
-      b.S = red[wt][y][lane][1];
-      b.U = red[wt][y][lane][2];
-      lm_merge(lo, tlo, b, red[wt][y][lane][3]);
-      if (j < p.n_tok) {
-        const float d = fmaf(lo.m, kLog2e, lo.c);
-        const float f = exp2_hw(-d);
-        bi_stats out;
-        out.max = lo.m;
-        out.sumexp = lo.S == 0.0f ? 0.0f : lo.S * f;
-        out.sumexp_logit = lo.S == 0.0f ? 0.0f : kLn2 * (fmaf(-d, lo.S, lo.U) * f);
-        out.target = bad ? NAN : tlo;
-        p.stats[tv * p.n_tok + j] = out;
-        if (bad && p.status_flag) atomicOr(p.status_flag, BI_FLAG_BAD_LABEL);
-      }
-    }
-    __syncthreads();
-  }
-}
-
-// One thread per row; chunks in ascending order (natural units).
-__global__ __launch_bounds__(256) void combine_kernel(const bi_stats* stats, int64_t n_chunks,
-                                                      int64_t n_rows, const int64_t* labels,
-                                                      int64_t ignore_index, float* logprob,
-                                                      float* entropy, float* lse_out) {
-  const int64_t row = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (row >= n_rows) return;
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(
+    const bi_stats* stats, int64_t n_chunks, int64_t n_rows, const int64_t* labels,
+    int64_t ignore_index, float* logprob, float* entropy, float* lse_out) {
+  const int q = threadIdx.x % kCombineLanes;
+  const int64_t row = int64_t(blockIdx.x) * (kCombineThreads / kCombineLanes) +
+                      threadIdx.x / kCombineLanes;
+  const bool live = row < n_rows;   // dead lanes still take part in the shuffles
   float M = -INFINITY;
-  for (int64_t c = 0; c < n_chunks; ++c) M = fmaxf(M, stats[c * n_rows + row].max);
+  if (live)
+    for (int64_t c = q; c < n_chunks; c += kCombineLanes) M = fmaxf(M, stats[c * n_rows + row].max);
+  M = xor_max(xor_max(xor_max(M, 1), 2), 4);
   float S = 0.0f, U = 0.0f, t = 0.0f;
-  for (int64_t c = 0; c < n_chunks; ++c) {
-    const bi_stats s = stats[c * n_rows + row];
-    t += s.target;
-    if (s.sumexp > 0.0f) {
-      const float gap = s.max - M;
-      const float a = exp2_hw(gap * kLog2e);
-      S = fmaf(a, s.sumexp, S);
-      U = fmaf(a, fmaf(gap, s.sumexp, s.sumexp_logit), U);
-    } else if (!(s.sumexp == 0.0f)) {   // NaN statistics propagate
-      S = NAN;
+  if (live)
+    for (int64_t c = q; c < n_chunks; c += kCombineLanes) {
+      const bi_stats s = stats[c * n_rows + row];
+      t += s.target;
+      if (s.sumexp > 0.0f) {
+        const float gap = s.max - M;
+        const float a = exp2_hw(gap * kLog2e);
+        S = fmaf(a, s.sumexp, S);
+        U = fmaf(a, fmaf(gap, s.sumexp, s.sumexp_logit), U);
+      } else if (!(s.sumexp == 0.0f)) {   // NaN statistics propagate
+        S = NAN;
+      }
     }
-  }
+  S = xor_add(xor_add(xor_add(S, 1), 2), 4);
+  U = xor_add(xor_add(xor_add(U, 1), 2), 4);
+  t = xor_add(xor_add(xor_add(t, 1), 2), 4);
+  if (!live || q != 0) return;
   const float lnS = kLn2 * log2_hw(S);
   const float lse = S == 0.0f ? -INFINITY : M + lnS;
   const int64_t y = labels[row];
@@ -1201,9 +893,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const bi_stats* stats, int
 
 // ------------------------------------------------------------- host side
 
-thread_local char g_err[512];
+}  // namespace
 
-int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+namespace bi_internal {
+
+namespace {
+thread_local char g_err[512];
+}
+
 int fail(int code, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
@@ -1217,9 +914,21 @@ int ok() {
   return BI_OK;
 }
 
-size_t elem_size(int dt) { return dt == BI_BF16 ? 2 : 4; }
-
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int launched(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(BI_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+const char* last_error() { return g_err; }
+
+}  // namespace bi_internal
+
+namespace {
+
+size_t elem_size(int dt) { return dt == BI_BF16 ? 2 : 4; }
 
 int check_dtype(int dt, const char* what) {
   if (dt != BI_F32 && dt != BI_BF16) return fail(BI_ERR_DTYPE, "%s: unknown dtype %d", what, dt);
@@ -1229,12 +938,6 @@ int check_dtype(int dt, const char* what) {
 unsigned grid_for(int64_t n_rows) {
   const int64_t cap = int64_t(1) << 30;
   return unsigned(n_rows < cap ? n_rows : cap);
-}
-
-int launched(const char* what) {
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(BI_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
-  return ok();
 }
 
 // every row of a [n_rows, row_bytes] array starting at p is 4-byte aligned
@@ -1317,7 +1020,7 @@ const char* bi_status_string(int status) {
   }
 }
 
-const char* bi_last_error(void) { return g_err; }
+const char* bi_last_error(void) { return last_error(); }
 
 int bi_row_geometry(int dtype, int64_t width, int* threads, int* elems_per_load,
                     int* loads_per_group) {
@@ -1503,45 +1206,6 @@ int bi_logprob_diff_stats(const float* a, const float* b, const int64_t* labels,
   return launched(fn);
 }
 
-int64_t bi_lmhead_tiles(int64_t n_vocab_rows) {
-  return n_vocab_rows <= 0 ? 0 : (n_vocab_rows + kLmTile - 1) / kLmTile;
-}
-
-int bi_lmhead_tile_stats(const void* hidden, const void* weight, int64_t n_tokens,
-                         int64_t n_vocab_rows, int64_t d, int64_t hidden_stride,
-                         int64_t weight_stride, int64_t vocab_offset, int64_t vocab,
-                         const int64_t* labels, int64_t ignore_index, bi_stats* stats,
-                         int32_t* status_flag, bi_stream_t stream) {
-  const char* fn = "bi_lmhead_tile_stats";
-  if (n_tokens < 0 || n_vocab_rows < 0)
-    return fail(BI_ERR_SHAPE, "%s: negative size", fn);
-  if (d < kLmBK || d % kLmBK != 0)
-    return fail(BI_ERR_SHAPE, "%s: d = %lld must be a positive multiple of %d", fn, (long long)d,
-                kLmBK);
-  if (hidden_stride < d || weight_stride < d || hidden_stride % 8 || weight_stride % 8)
-    return fail(BI_ERR_SHAPE, "%s: strides must be >= d and multiples of 8 elements", fn);
-  if (vocab < 1 || vocab_offset < 0 || vocab_offset + n_vocab_rows > vocab)
-    return fail(BI_ERR_SHAPE, "%s: rows [%lld, %lld) outside the vocabulary [0, %lld)", fn,
-                (long long)vocab_offset, (long long)(vocab_offset + n_vocab_rows),
-                (long long)vocab);
-  if (n_tokens == 0 || n_vocab_rows == 0) return ok();
-  if (!hidden || !weight || !labels || !stats)
-    return fail(BI_ERR_NULL, "%s: hidden, weight, labels and stats are required", fn);
-  if (!aligned(hidden, 16) || !aligned(weight, 16) || !aligned(labels, 8) ||
-      !aligned(stats, 16) || !aligned(status_flag, 4))
-    return fail(BI_ERR_ALIGN, "%s: hidden and weight need 16-byte alignment", fn);
-  LmArgs a{static_cast<const uint16_t*>(hidden), static_cast<const uint16_t*>(weight),
-           n_tokens, n_vocab_rows, d, hidden_stride, weight_stride, vocab_offset, vocab,
-           labels, ignore_index, stats, status_flag, bi_lmhead_tiles(n_vocab_rows),
-           (n_tokens + kLmTile - 1) / kLmTile};
-  const int64_t total = a.tiles_v * a.tiles_n;
-  const int64_t blocks = 8 * ((total + 7) / 8);
-  if (blocks > 0x7fffffff) return fail(BI_ERR_SHAPE, "%s: too many tiles", fn);
-  hipLaunchKernelGGL(lmhead_stats_kernel, dim3(unsigned(blocks)), dim3(kLmThreads), 0,
-                     static_cast<hipStream_t>(stream), a);
-  return launched(fn);
-}
-
 int bi_stats_combine(const bi_stats* stats, int64_t n_chunks, int64_t n_rows,
                      const int64_t* labels, int64_t ignore_index, float* logprob,
                      float* entropy, float* lse, bi_stream_t stream) {
@@ -1554,10 +1218,10 @@ int bi_stats_combine(const bi_stats* stats, int64_t n_chunks, int64_t n_rows,
   if (!aligned(stats, 4) || !aligned(labels, 8) || !aligned(logprob, 4) || !aligned(entropy, 4) ||
       !aligned(lse, 4))
     return fail(BI_ERR_ALIGN, "%s: misaligned pointer", fn);
-  const unsigned threads = 256;
-  const int64_t blocks = (n_rows + threads - 1) / threads;
+  const int64_t rows_per_block = kCombineThreads / kCombineLanes;
+  const int64_t blocks = (n_rows + rows_per_block - 1) / rows_per_block;
   if (blocks > 0x7fffffff) return fail(BI_ERR_SHAPE, "%s: too many rows", fn);
-  hipLaunchKernelGGL(combine_kernel, dim3(unsigned(blocks)), dim3(threads), 0,
+  hipLaunchKernelGGL(combine_kernel, dim3(unsigned(blocks)), dim3(kCombineThreads), 0,
                      static_cast<hipStream_t>(stream), stats, n_chunks, n_rows, labels,
                      ignore_index, logprob, entropy, lse);
   return launched(fn);

@@ -206,12 +206,16 @@ BI_API int bi_vocab_chunk_stats(const void* logits_chunk, int dtype, int64_t n_r
                          const int64_t* labels, int64_t ignore_index,
                          bi_stats* stats, int32_t* status_flag, bi_stream_t stream);
 
-/* Exact combine of chunk statistics, chunks taken in ascending order.
+/* Exact combine of chunk statistics.
  * Defined in PR #4685, Why, and the reply "Batch invariance under the
- * patched logprob path", Q2: M = max_c m_c is exact; then, for c = 0, 1, ...,
- * S += e^(m_c - M) S_c, U += e^(m_c - M) (U_c + (m_c - M) S_c), t += t_c;
- * a chunk with S_c == 0 contributes nothing.  lse = M + ln S,
+ * patched logprob path", Q2: M = max_c m_c is exact; then
+ * S = sum_c e^(m_c - M) S_c, U = sum_c e^(m_c - M) (U_c + (m_c - M) S_c),
+ * t = sum_c t_c; a chunk with S_c == 0 contributes nothing.  lse = M + ln S,
  * logprob = t - lse (+0.0 if ignored), entropy = ln S - U / S.
+ * Summation order (fixed by n_chunks alone, hence batch-invariant): chunk c
+ * goes to partial sum c mod 8, each partial sum takes its chunks in ascending
+ * order, and the 8 partial sums are added pairwise by an xor butterfly
+ * (partners at distance 1, then 2, then 4).
  *   stats    [n_chunks][n_rows] bi_stats (chunk-major)
  *   n_chunks >= 1
  *   logprob, entropy, lse  [n_rows] fp32 each; any may be NULL, not all
@@ -253,16 +257,17 @@ BI_API int bi_logprob_diff_stats(const float* a, const float* b, const int64_t* 
  * computed on the matrix cores (bf16 inputs, fp32 accumulation) and reduced
  * straight to bi_stats per token, so the logits never reach memory (the
  * chunked lm_head of "ZeroSyncGRPOTrainer - #6949"; shard-local statistics,
- * PR #4685 Why).  Rows are cut into tiles of 128; tile c of token n is
+ * PR #4685 Why).  Rows are cut into tiles of 256; tile c of token n is
  * written to stats[c * n_tokens + n], with the same meaning as
- * bi_vocab_chunk_stats on those 128 columns.  bi_stats_combine over the
+ * bi_vocab_chunk_stats on those 256 columns.  bi_stats_combine over the
  * bi_lmhead_tiles(n_vocab_rows) tiles then yields logprob, entropy and lse.
  * Each logit is the same MFMA sequence whatever n_tokens is (batch-
  * invariant).  The fp32 logits are used as computed (not rounded to bf16).
  *   hidden  [n_tokens, hidden_stride] bf16, 16-byte aligned rows
  *   weight  [n_vocab_rows, weight_stride] bf16 (the lm_head rows of global
  *           vocabulary ids vocab_offset .. vocab_offset + n_vocab_rows - 1)
- *   d       hidden size, a positive multiple of 64; strides multiples of 8
+ *   d       hidden size, a positive multiple of 64 (at most 2^24); strides
+ *           multiples of 8
  *   stats   [bi_lmhead_tiles(n_vocab_rows)][n_tokens] bi_stats, 16-byte aligned
  */
 BI_API int bi_lmhead_tile_stats(const void* hidden, const void* weight, int64_t n_tokens,
@@ -271,8 +276,13 @@ BI_API int bi_lmhead_tile_stats(const void* hidden, const void* weight, int64_t 
                                 const int64_t* labels, int64_t ignore_index, bi_stats* stats,
                                 int32_t* status_flag, bi_stream_t stream);
 
-/* Number of 128-row tiles bi_lmhead_tile_stats writes for n_vocab_rows rows. */
+/* Number of tiles bi_lmhead_tile_stats writes for n_vocab_rows rows: tile t
+ * covers rows t * bi_lmhead_tile_rows() .. (t + 1) * bi_lmhead_tile_rows() - 1
+ * (the last one clipped). */
 BI_API int64_t bi_lmhead_tiles(int64_t n_vocab_rows);
+
+/* lm_head rows per statistics tile of bi_lmhead_tile_stats (256). */
+BI_API int64_t bi_lmhead_tile_rows(void);
 
 /* Human-readable name of a status code (static string). */
 BI_API const char* bi_status_string(int status);

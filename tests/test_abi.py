@@ -36,7 +36,8 @@ def test_header_declares_the_four_entry_points():
     names = declared_functions()
     for fn in ("bi_logprob_fwd", "bi_logprob_bwd", "bi_vocab_chunk_stats", "bi_stats_combine",
                "bi_logprob_fwd_bwd", "bi_policy_loss_fwd_bwd", "bi_logprob_fwd_multi",
-               "bi_logprob_diff_stats", "bi_lmhead_tile_stats", "bi_lmhead_tiles"):
+               "bi_logprob_diff_stats", "bi_lmhead_tile_stats", "bi_lmhead_tiles",
+               "bi_lmhead_tile_rows"):
         assert fn in names
 
 
@@ -150,12 +151,17 @@ def test_lmhead_argument_errors(L):
                  a["lab"], -100, a["st"], NUL, NUL)
 
     assert call(d=100) == bi.BI_ERR_SHAPE        # not a multiple of 64
+    assert call(d=96) == bi.BI_ERR_SHAPE
+    assert call(d=0) == bi.BI_ERR_SHAPE
     assert call(ldh=130) == bi.BI_ERR_SHAPE      # stride not a multiple of 8
     assert call(off=10) == bi.BI_ERR_SHAPE       # rows past the vocabulary
     assert call(h=NUL) == bi.BI_ERR_NULL
     assert call(w=ctypes.c_void_p(0x10008)) == bi.BI_ERR_ALIGN
     assert call(n=0, h=NUL, w=NUL, lab=NUL, st=NUL) == bi.BI_OK
-    assert L.bi_lmhead_tiles(300) == 3 and L.bi_lmhead_tiles(128) == 1 and L.bi_lmhead_tiles(0) == 0
+    t = L.bi_lmhead_tile_rows()
+    assert t == 256
+    assert L.bi_lmhead_tiles(300) == 2 and L.bi_lmhead_tiles(t) == 1 and L.bi_lmhead_tiles(0) == 0
+    assert L.bi_lmhead_tiles(t + 1) == 2
 
 
 def chunk(L, logits=P, dtype=bi.BI_BF16, n=4, w=25, rs=100, off=25, v=100, labels=P,

@@ -1,7 +1,7 @@
 """GPU parity of the lm_head projection fused with the statistics.
 
 bi_lmhead_tile_stats computes the logits hidden @ weight^T on the matrix cores
-and reduces them to per-token statistics of 128-row tiles; bi_stats_combine
+and reduces them to per-token statistics of 256-row tiles; bi_stats_combine
 finishes.  Checked against the fp64 oracle (exact float64 products of the bf16
 inputs): per-tile statistics, and the combined logprob / entropy / lse within
 2e-4 (the logits are fp32 accumulations of exact bf16 products, so the
@@ -35,6 +35,7 @@ def check_tiles(st, ost):
 
 
 @pytest.mark.parametrize("n,vc,d", [(300, 1000, 128), (128, 128, 64), (77, 333, 256),
+                                    (64, 1, 64), (513, 257, 192),
                                     (1000, 4099, 512), (5, 130, 64)])
 def test_tiles_and_combine_against_oracle(n, vc, d):
     b = wl.lmhead_batch(n, vc, d, seed=n + vc + d, ignore_frac=0.1)
@@ -46,7 +47,7 @@ def test_tiles_and_combine_against_oracle(n, vc, d):
     assert int(flag.item()) == 0
     h = orc.decode(b.hidden, "bf16")
     w = orc.decode(b.weight, "bf16")
-    check_tiles(host(st), orc.lmhead_tile_stats(h, w, b.labels, 0, vc, 128))
+    check_tiles(host(st), orc.lmhead_tile_stats(h, w, b.labels, 0, vc, bi.lmhead_tile_rows()))
     olp, oent, olse = orc.forward(orc.lmhead_logits(h, w), b.labels)
     assert_close(host(lp), olp, TOL, "logprob")
     assert_close(host(ent), oent, TOL, "entropy")

@@ -155,7 +155,9 @@ def test_chunk_and_multi_paths_are_batch_invariant():
             ids = torch.stack([labels, torch.zeros_like(labels), labels.flip(0)], dim=1)
             mlp, _, _ = bi.fwd_multi(logits, ids.contiguous())
             pos = torch.from_numpy(case.positions).cuda()
-            outs.append((st[:, pos].reshape(-1), clp[pos], cent[pos], clse[pos], mlp[pos, :2].reshape(-1)))
+            # statistics row-major ([row, chunk, 4]) so that cases concatenate in row order
+            outs.append((st[:, pos].transpose(0, 1).reshape(-1), clp[pos], cent[pos], clse[pos],
+                         mlp[pos, :2].reshape(-1)))
         torch.cuda.synchronize()
         per_n[n] = [torch.cat([o[k] for o in outs]) for k in range(5)]
     ref = per_n[1]
