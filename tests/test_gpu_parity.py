@@ -252,6 +252,34 @@ def test_fused_equals_fwd_then_bwd_bitwise(V, dt, gdt):
     check_against_oracle(b, (host(flp), host(fent), host(flse)), grads)
 
 
+@pytest.mark.parametrize("V", [131_080, 151_938, 155_640, 155_648])
+@pytest.mark.parametrize("gdt", [torch.bfloat16, torch.float32], ids=["g_bf16", "g_f32"])
+def test_fused_wide_rows_tail_cases_equal_two_calls(V, gdt):
+    # widths around the headline vocabulary (bf16 rows of 1024 lanes, 17 to 19
+    # vectors per lane): a ragged last step with a whole or a partial vector,
+    # or none; labels in the first column, the last column, the last whole
+    # vector, ignored and out of range
+    n = 8
+    b = random_batch(n, V, "bf16", seed=V, ignore_frac=0.0)
+    labels = b.labels.copy()
+    labels[:6] = [0, V - 1, V - 2, (V // 8) * 8 - 1, -100, V + 5]
+    logits, lab = dev_logits(b.logits, "bf16"), dev(labels)
+    for w in (dev(b.weights), None):
+        _fused_vs_two_calls(logits, lab, w, gdt)
+    ok = labels[:] != V + 5
+    lp, ent, lse, g = bi.fwd_bwd(logits, lab, dev(b.weights), gdt)
+    torch.cuda.synchronize()
+    rows = np.flatnonzero(ok)
+    z = orc.decode(b.logits[rows], "bf16")
+    olp, oent, olse = orc.forward(z, labels[rows])
+    tl, te, tg = TOL["bf16"]
+    assert_close(host(lp)[rows], olp, tl, "logprob")
+    assert_close(host(ent)[rows], oent, te, "entropy")
+    og = orc.backward(z, labels[rows], olse, b.weights[rows])
+    gh = host(g.float())[rows]
+    assert np.all(np.abs(gh - og) <= tg + (0.5 * ulp_bf16(og) if gdt == torch.bfloat16 else 0))
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("pad,offset", [(1, 0), (3, 1)])
 def test_fused_on_strided_unaligned_rows(dt, pad, offset):
