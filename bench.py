@@ -62,17 +62,22 @@ KERNEL_SOURCES = [os.path.join(ROOT, "entropy_bi_logprob_amd", "csrc", f)
                   for f in ("bi_common.h", "bi_logprob.hip")]
 
 
-def measured_traffic(kernel):
-    """HBM bytes per launch from the committed counter summary, or None when the
+LMHEAD_SUMMARY = os.path.join(ROOT, "profiles", "lmhead_32768x2560x151936_bf16_counters.md")
+LMHEAD_SOURCES = [os.path.join(ROOT, "entropy_bi_logprob_amd", "csrc", f)
+                  for f in ("bi_common.h", "bi_lmhead.hip")]
+
+
+def measured_traffic(kernel, summary=TRAFFIC_SUMMARY, sources=KERNEL_SOURCES):
+    """HBM bytes per launch from a committed counter summary, or None when the
     kernel source has changed since the counters were taken."""
     import hashlib
     import re
 
     try:
-        text = open(TRAFFIC_SUMMARY).read()
+        text = open(summary).read()
         block = json.loads(re.search(r"```json\n(.*?)\n```", text, re.S).group(1))
         h = hashlib.sha256()
-        for f in KERNEL_SOURCES:
+        for f in sources:
             h.update(open(f, "rb").read())
         sha = h.hexdigest()
     except (OSError, AttributeError, ValueError):
@@ -127,7 +132,9 @@ def lmhead_leg(bi, torch, np, wl, N, V, seed, steps, warm, stream):
             "fused_ms": t_stats + t_comb, "tile_stats_ms": t_stats, "combine_ms": t_comb,
             "rows_per_s": N / ((t_stats + t_comb) * 1e-3),
             "roofline": {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": tf / MFMA_BF16_PEAK_TFLOPS, "traffic": None},
+                         "unit": "TFLOP/s", "frac": tf / MFMA_BF16_PEAK_TFLOPS,
+                         "traffic": (measured_traffic("lmhead", LMHEAD_SUMMARY, LMHEAD_SOURCES)
+                                     if (N, V, d) == (32768, 151936, 2560) else None)},
             "unfused_ms": t_gemm + t_fwd, "unfused_gemm_ms": t_gemm, "unfused_fwd_ms": t_fwd,
             "unfused_gemm_TFLOPs": flops / (t_gemm * 1e-3) / 1e12,
             "speedup_vs_unfused": (t_gemm + t_fwd) / (t_stats + t_comb)}
