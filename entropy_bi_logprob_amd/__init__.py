@@ -23,7 +23,7 @@ import torch  # first: the library then binds to the HIP runtime torch has loade
 __all__ = [
     "IGNORE_INDEX", "BiError", "fwd", "bwd", "fwd_bwd", "policy_loss_fwd_bwd", "vocab_chunk_stats", "stats_combine",
     "row_geometry", "fwd_multi", "diff_stats", "lmhead_tile_stats", "lmhead_logprob",
-    "lmhead_tile_rows",
+    "lmhead_tile_rows", "lmhead_grad_logits", "lmhead_backward", "lmhead_logprob_entropy",
     "LogprobEntropy", "logprob_entropy", "lib",
     "library_path",
 ]
@@ -96,6 +96,14 @@ def lib() -> ctypes.CDLL:
     L.bi_lmhead_tiles.restype = i64
     L.bi_lmhead_tile_rows.argtypes = []
     L.bi_lmhead_tile_rows.restype = i64
+    L.bi_lmhead_grad_logits.argtypes = [vp, vp, i64, i64, i64, i64, i64, i64, i64, vp, i64, vp,
+                                        vp, vp, i64, vp, vp]
+    L.bi_lmhead_grad_logits.restype = i32
+    L.bi_lmhead_backward.argtypes = [vp, vp, i64, i64, i64, i64, i64, i64, i64, vp, i64, vp, vp,
+                                     vp, i64, vp, i32, i64, vp, i64, vp, vp]
+    L.bi_lmhead_backward.restype = i32
+    L.bi_lmhead_backward_workspace.argtypes = [i64, i64]
+    L.bi_lmhead_backward_workspace.restype = i64
     L.bi_stats_combine.argtypes = [vp, i64, i64, vp, i64, vp, vp, vp, vp]
     L.bi_row_geometry.argtypes = [i32, i64, ctypes.POINTER(i32), ctypes.POINTER(i32),
                                   ctypes.POINTER(i32)]
@@ -379,6 +387,77 @@ def lmhead_logprob(hidden: torch.Tensor, weight: torch.Tensor, labels: torch.Ten
     return stats_combine(st, labels, ignore_index, stream=stream)
 
 
+def _lmhead_operands(hidden, weight, labels):
+    n, d, ldh = _rows(hidden, "hidden")
+    vc, dw, ldw = _rows(weight, "weight")
+    if hidden.dtype != torch.bfloat16 or weight.dtype != torch.bfloat16 or d != dw:
+        raise ValueError("hidden [N, d] and weight [Vc, d] must be bfloat16 with the same d")
+    _vec(labels, n, torch.int64, "labels")
+    return n, d, ldh, vc, ldw
+
+
+def lmhead_grad_logits(hidden: torch.Tensor, weight: torch.Tensor, labels: torch.Tensor,
+                       lse: torch.Tensor, token_weights: Optional[torch.Tensor] = None,
+                       vocab_offset: int = 0, vocab: Optional[int] = None,
+                       ignore_index: int = IGNORE_INDEX, *, out: Optional[torch.Tensor] = None,
+                       status: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """[Vc, N] bf16 gradient of the lm_head logits, vocabulary-major:
+    w_n * (softmax(z_n)[v] - [v == y_n]) with the logits recomputed."""
+    n, d, ldh, vc, ldw = _lmhead_operands(hidden, weight, labels)
+    _vec(lse, n, torch.float32, "lse")
+    _vec(token_weights, n, torch.float32, "token_weights")
+    _vec(status, 1, torch.int32, "status")
+    vocab = vocab_offset + vc if vocab is None else vocab
+    if out is None:
+        out = torch.empty((vc, n), dtype=torch.bfloat16, device=hidden.device)
+    _, ncols, ldg = _rows(out, "out")
+    if out.dtype != torch.bfloat16 or out.shape[0] != vc or ncols != n:
+        raise ValueError(f"out must be a bfloat16 [{vc}, {n}] tensor")
+    _check("bi_lmhead_grad_logits", lib().bi_lmhead_grad_logits(
+        _ptr(hidden), _ptr(weight), n, vc, d, ldh, ldw, vocab_offset, vocab, _ptr(labels),
+        ignore_index, _ptr(lse), _ptr(token_weights), _ptr(out), ldg, _ptr(status),
+        _stream(stream)))
+    return out
+
+
+def lmhead_backward(hidden: torch.Tensor, weight: torch.Tensor, labels: torch.Tensor,
+                    lse: torch.Tensor, token_weights: Optional[torch.Tensor] = None,
+                    vocab_offset: int = 0, vocab: Optional[int] = None,
+                    ignore_index: int = IGNORE_INDEX, *, grad_hidden: Optional[torch.Tensor] = None,
+                    grad_weight: Optional[torch.Tensor] = None,
+                    grad_weight_dtype: torch.dtype = torch.bfloat16, chunk_rows: int = 16384,
+                    workspace: Optional[torch.Tensor] = None,
+                    status: Optional[torch.Tensor] = None, stream=None):
+    """(grad_hidden fp32 [N, d], grad_weight [Vc, d]) of sum_n w_n * CE_n through the
+    lm_head, from the saved lse.  grad_hidden is accumulated into when given."""
+    n, d, ldh, vc, ldw = _lmhead_operands(hidden, weight, labels)
+    _vec(lse, n, torch.float32, "lse")
+    _vec(token_weights, n, torch.float32, "token_weights")
+    _vec(status, 1, torch.int32, "status")
+    vocab = vocab_offset + vc if vocab is None else vocab
+    dev = hidden.device
+    if grad_hidden is None:
+        grad_hidden = torch.zeros((n, d), dtype=torch.float32, device=dev)
+    _, dh, ldgh = _rows(grad_hidden, "grad_hidden")
+    if grad_hidden.dtype != torch.float32 or grad_hidden.shape[0] != n or dh != d:
+        raise ValueError(f"grad_hidden must be a float32 [{n}, {d}] tensor")
+    if grad_weight is None:
+        grad_weight = torch.empty((vc, d), dtype=grad_weight_dtype, device=dev)
+    _, dgw, ldgw = _rows(grad_weight, "grad_weight")
+    if grad_weight.shape[0] != vc or dgw != d:
+        raise ValueError(f"grad_weight must be a [{vc}, {d}] tensor")
+    L = lib()
+    if workspace is None:
+        nbytes = int(L.bi_lmhead_backward_workspace(n, min(chunk_rows, max(vc, 1))))
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    _check("bi_lmhead_backward", L.bi_lmhead_backward(
+        _ptr(hidden), _ptr(weight), n, vc, d, ldh, ldw, vocab_offset, vocab, _ptr(labels),
+        ignore_index, _ptr(lse), _ptr(token_weights), _ptr(grad_hidden), ldgh,
+        _ptr(grad_weight), _dtype_code(grad_weight.dtype), ldgw, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(status), _stream(stream)))
+    return grad_hidden, grad_weight
+
+
 def row_geometry(dtype: torch.dtype, width: int) -> Tuple[int, int, int]:
     """(threads per workgroup, elements per 16-byte load, loads per rescale group)."""
     a, b, c = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
@@ -414,3 +493,30 @@ class LogprobEntropy(torch.autograd.Function):
 def logprob_entropy(logits, labels, ignore_index=IGNORE_INDEX, grad_dtype=None):
     """Autograd-aware (logprob, entropy) of full rows."""
     return LogprobEntropy.apply(logits, labels, ignore_index, grad_dtype)
+
+
+class LmHeadLogprobEntropy(torch.autograd.Function):
+    """logprob (differentiable in hidden and weight) and entropy (a metric) of the
+    lm_head logits hidden @ weight^T, which are never materialised."""
+
+    @staticmethod
+    def forward(ctx, hidden, weight, labels, ignore_index=IGNORE_INDEX, chunk_rows=16384):
+        lp, ent, lse = lmhead_logprob(hidden, weight, labels, ignore_index)
+        ctx.save_for_backward(hidden, weight, labels, lse)
+        ctx.ignore_index = ignore_index
+        ctx.chunk_rows = chunk_rows
+        ctx.mark_non_differentiable(ent)
+        return lp, ent
+
+    @staticmethod
+    def backward(ctx, grad_lp, grad_ent):
+        hidden, weight, labels, lse = ctx.saved_tensors
+        w = (-grad_lp).to(torch.float32).contiguous()   # d logprob / d z = onehot - softmax
+        gh, gw = lmhead_backward(hidden, weight, labels, lse, w, 0, None, ctx.ignore_index,
+                                 grad_weight_dtype=weight.dtype, chunk_rows=ctx.chunk_rows)
+        return gh.to(hidden.dtype), gw, None, None, None
+
+
+def lmhead_logprob_entropy(hidden, weight, labels, ignore_index=IGNORE_INDEX, chunk_rows=16384):
+    """Autograd-aware (logprob, entropy) straight from hidden states and lm_head rows."""
+    return LmHeadLogprobEntropy.apply(hidden, weight, labels, ignore_index, chunk_rows)

@@ -3,7 +3,8 @@
     python -m entropy_bi_logprob_amd.build
 
 The library is a plain C ABI (include/bi_logprob.h) around hand-written HIP
-kernels; it links only the HIP runtime.
+kernels; it links the HIP runtime and rocBLAS (the lm_head backward's two
+plain GEMMs).
 """
 from __future__ import annotations
 
@@ -14,7 +15,10 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SOURCES = [os.path.join(PKG, "csrc", f) for f in ("bi_logprob.hip", "bi_lmhead.hip")]
+SOURCES = [os.path.join(PKG, "csrc", f)
+           for f in ("bi_logprob.hip", "bi_lmhead.hip", "bi_lmhead_bwd.hip")]
+# the lm_head backward's two plain GEMMs are rocBLAS calls
+LIBS = ["-L/opt/rocm/lib", "-lrocblas"]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libbi_logprob.so")
 ARCH = "gfx950"
@@ -40,7 +44,7 @@ def hipcc() -> str:
 def build(verbose: bool = False, extra_flags=(), out: str = LIB) -> str:
     """Compile the HIP library into ``out``; returns its path."""
     tmp = out + ".tmp"
-    cmd = [hipcc(), *FLAGS, *extra_flags, "-I", INCLUDE, "-o", tmp, *SOURCES]
+    cmd = [hipcc(), *FLAGS, *extra_flags, "-I", INCLUDE, "-o", tmp, *SOURCES, *LIBS]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

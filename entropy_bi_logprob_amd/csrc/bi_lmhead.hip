@@ -110,9 +110,13 @@ struct LmArgs {
   int64_t vocab_offset, vocab;
   const int64_t* labels;
   int64_t ignore_index;
-  bi_stats* stats;          // [tiles_v][n_tok]
+  bi_stats* stats;          // [tiles_v][n_tok]          (statistics kernel)
   int32_t* status_flag;
   int64_t tiles_v, tiles_n;
+  const float* lse;         // [n_tok]                   (grad-logits kernel)
+  const float* token_weights;   // [n_tok] or NULL (= 1)
+  uint16_t* gout;           // [n_voc, ldg] bf16 bits: gradient of the logits, vocabulary-major
+  int64_t ldg;
 };
 
 // Tile (tv, tn) of workgroup b; false for the padding workgroups of the grid.
@@ -255,8 +259,13 @@ __device__ inline void lm_merge(Acc& a, float& ta, const Acc& b, float tb) {
   ta = ta + tb;
 }
 
+// GRAD = false: per-token statistics of each 256-row vocabulary tile.
+// GRAD = true:  the gradient of the logits, w * (softmax - onehot) from the
+// saved lse, written as bf16 (the cross-entropy backward of PR #4685
+// Summary, on the lm_head logits).  Same main loop, same logits bits.
+template <bool GRAD>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEU, kWavesPerEU)))
-void lmhead_stats_kernel(LmArgs p) {
+void lmhead_kernel(LmArgs p) {
   __shared__ __attribute__((aligned(1024))) char ring[kRing * kStageBytes];
   __shared__ float red[kWT][kYB][32][4];
   int64_t tv, tn;
@@ -341,9 +350,47 @@ void lmhead_stats_kernel(LmArgs p) {
   }
   wait_counts<0, 15>();   // no request may still be writing LDS when the workgroup ends
 
+  const int64_t wrow0 = v0 + kWV * wv;     // first vocabulary row of this wave
+  if constexpr (GRAD) {
+    // gradient of the logits: w * (p - [v == y]), p = 2^((z - lse) * log2e)
+    // as the row backward computes it; +0 for ignored tokens, NaN for bad
+    // labels.  Vocabulary-major bf16: lanes write consecutive tokens.
+#pragma unroll
+    for (int y = 0; y < kYB; ++y) {
+      const int64_t j = n0 + kWN * wt + 32 * y + lr;
+      if (j >= p.n_tok) continue;
+      const int64_t lb = lab[y];
+      const bool ignored = lb == p.ignore_index;
+      const bool bad = !ignored && (lb < 0 || lb >= p.vocab);
+      const float lse = p.lse[j];
+      const float w = p.token_weights ? p.token_weights[j] : 1.0f;
+      const int64_t yl = lb - p.vocab_offset;   // the label's row among these lm_head rows
+#pragma unroll
+      for (int x = 0; x < kXB; ++x)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t i = wrow0 + 32 * x + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (i < p.n_voc) {
+            float g;
+            if (ignored) {
+              g = 0.0f;
+            } else if (bad) {
+              g = NAN;
+            } else {
+              const float pr = exp2_hw((acc[x][y][r] - lse) * kLog2e);
+              g = i == yl ? w * (pr - 1.0f) : w * pr;
+            }
+            reinterpret_cast<__bf16*>(p.gout)[i * p.ldg + j] = __bf16(g);
+          }
+        }
+      if (bad && p.status_flag && tv == 0 && wv == 0 && half == 0)
+        atomicOr(p.status_flag, BI_FLAG_BAD_LABEL);
+    }
+    return;
+  }
+
   // epilogue: statistics of each token over this tile's 256 vocabulary rows
   const bool full = v0 + kTV <= p.n_voc;   // uniform: no row of the tile is masked
-  const int64_t wrow0 = v0 + kWV * wv;     // first vocabulary row of this wave
   float tl[kYB];
   Acc lo[kYB];
 #pragma unroll
@@ -419,6 +466,54 @@ void lmhead_stats_kernel(LmArgs p) {
   }
 }
 
+// Shared validation of the lm_head entry points; fills the common arguments.
+int lm_setup(const char* fn, LmArgs* a, const void* hidden, const void* weight, int64_t n_tokens,
+             int64_t n_vocab_rows, int64_t d, int64_t hidden_stride, int64_t weight_stride,
+             int64_t vocab_offset, int64_t vocab, const int64_t* labels, int64_t ignore_index,
+             int32_t* status_flag) {
+  if (n_tokens < 0 || n_vocab_rows < 0) return fail(BI_ERR_SHAPE, "%s: negative size", fn);
+  if (d < kBK || d % kBK != 0 || d > (int64_t(1) << 24))
+    return fail(BI_ERR_SHAPE, "%s: d = %lld must be a positive multiple of %d (at most 2^24)",
+                fn, (long long)d, kBK);
+  if (hidden_stride < d || weight_stride < d || hidden_stride % 8 || weight_stride % 8)
+    return fail(BI_ERR_SHAPE, "%s: strides must be >= d and multiples of 8 elements", fn);
+  if (vocab < 1 || vocab_offset < 0 || vocab_offset + n_vocab_rows > vocab)
+    return fail(BI_ERR_SHAPE, "%s: rows [%lld, %lld) outside the vocabulary [0, %lld)", fn,
+                (long long)vocab_offset, (long long)(vocab_offset + n_vocab_rows),
+                (long long)vocab);
+  if (n_tokens == 0 || n_vocab_rows == 0) return BI_OK;
+  if (!hidden || !weight || !labels)
+    return fail(BI_ERR_NULL, "%s: hidden, weight and labels are required", fn);
+  if (!aligned(hidden, 16) || !aligned(weight, 16) || !aligned(labels, 8) ||
+      !aligned(status_flag, 4))
+    return fail(BI_ERR_ALIGN, "%s: hidden and weight need 16-byte alignment", fn);
+  a->hidden = static_cast<const uint16_t*>(hidden);
+  a->weight = static_cast<const uint16_t*>(weight);
+  a->n_tok = n_tokens;
+  a->n_voc = n_vocab_rows;
+  a->d = d;
+  a->ldh = hidden_stride;
+  a->ldw = weight_stride;
+  a->vocab_offset = vocab_offset;
+  a->vocab = vocab;
+  a->labels = labels;
+  a->ignore_index = ignore_index;
+  a->status_flag = status_flag;
+  a->tiles_v = (n_vocab_rows + kTV - 1) / kTV;
+  a->tiles_n = (n_tokens + kTN - 1) / kTN;
+  return BI_OK;
+}
+
+template <bool GRAD>
+int lm_launch(const char* fn, const LmArgs& a, bi_stream_t stream) {
+  const int64_t total = a.tiles_v * a.tiles_n;
+  const int64_t blocks = 8 * ((total + 7) / 8);
+  if (blocks > 0x7fffffff) return fail(BI_ERR_SHAPE, "%s: too many tiles", fn);
+  hipLaunchKernelGGL(lmhead_kernel<GRAD>, dim3(unsigned(blocks)), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), a);
+  return launched(fn);
+}
+
 }  // namespace
 
 extern "C" {
@@ -435,33 +530,40 @@ int bi_lmhead_tile_stats(const void* hidden, const void* weight, int64_t n_token
                          const int64_t* labels, int64_t ignore_index, bi_stats* stats,
                          int32_t* status_flag, bi_stream_t stream) {
   const char* fn = "bi_lmhead_tile_stats";
-  if (n_tokens < 0 || n_vocab_rows < 0)
-    return fail(BI_ERR_SHAPE, "%s: negative size", fn);
-  if (d < kBK || d % kBK != 0 || d > (int64_t(1) << 24))
-    return fail(BI_ERR_SHAPE, "%s: d = %lld must be a positive multiple of %d (at most 2^24)",
-                fn, (long long)d, kBK);
-  if (hidden_stride < d || weight_stride < d || hidden_stride % 8 || weight_stride % 8)
-    return fail(BI_ERR_SHAPE, "%s: strides must be >= d and multiples of 8 elements", fn);
-  if (vocab < 1 || vocab_offset < 0 || vocab_offset + n_vocab_rows > vocab)
-    return fail(BI_ERR_SHAPE, "%s: rows [%lld, %lld) outside the vocabulary [0, %lld)", fn,
-                (long long)vocab_offset, (long long)(vocab_offset + n_vocab_rows),
-                (long long)vocab);
+  LmArgs a{};
+  if (int r = lm_setup(fn, &a, hidden, weight, n_tokens, n_vocab_rows, d, hidden_stride,
+                       weight_stride, vocab_offset, vocab, labels, ignore_index, status_flag))
+    return r;
   if (n_tokens == 0 || n_vocab_rows == 0) return ok();
-  if (!hidden || !weight || !labels || !stats)
-    return fail(BI_ERR_NULL, "%s: hidden, weight, labels and stats are required", fn);
-  if (!aligned(hidden, 16) || !aligned(weight, 16) || !aligned(labels, 8) ||
-      !aligned(stats, 16) || !aligned(status_flag, 4))
-    return fail(BI_ERR_ALIGN, "%s: hidden and weight need 16-byte alignment", fn);
-  LmArgs a{static_cast<const uint16_t*>(hidden), static_cast<const uint16_t*>(weight),
-           n_tokens, n_vocab_rows, d, hidden_stride, weight_stride, vocab_offset, vocab,
-           labels, ignore_index, stats, status_flag, bi_lmhead_tiles(n_vocab_rows),
-           (n_tokens + kTN - 1) / kTN};
-  const int64_t total = a.tiles_v * a.tiles_n;
-  const int64_t blocks = 8 * ((total + 7) / 8);
-  if (blocks > 0x7fffffff) return fail(BI_ERR_SHAPE, "%s: too many tiles", fn);
-  hipLaunchKernelGGL(lmhead_stats_kernel, dim3(unsigned(blocks)), dim3(kThreads), 0,
-                     static_cast<hipStream_t>(stream), a);
-  return launched(fn);
+  if (!stats) return fail(BI_ERR_NULL, "%s: stats is required", fn);
+  if (!aligned(stats, 16)) return fail(BI_ERR_ALIGN, "%s: stats needs 16-byte alignment", fn);
+  a.stats = stats;
+  return lm_launch<false>(fn, a, stream);
+}
+
+int bi_lmhead_grad_logits(const void* hidden, const void* weight, int64_t n_tokens,
+                          int64_t n_vocab_rows, int64_t d, int64_t hidden_stride,
+                          int64_t weight_stride, int64_t vocab_offset, int64_t vocab,
+                          const int64_t* labels, int64_t ignore_index, const float* lse,
+                          const float* token_weights, void* grad_logits, int64_t grad_stride,
+                          int32_t* status_flag, bi_stream_t stream) {
+  const char* fn = "bi_lmhead_grad_logits";
+  LmArgs a{};
+  if (int r = lm_setup(fn, &a, hidden, weight, n_tokens, n_vocab_rows, d, hidden_stride,
+                       weight_stride, vocab_offset, vocab, labels, ignore_index, status_flag))
+    return r;
+  if (grad_stride < n_tokens)
+    return fail(BI_ERR_SHAPE, "%s: grad_stride %lld < n_tokens %lld", fn, (long long)grad_stride,
+                (long long)n_tokens);
+  if (n_tokens == 0 || n_vocab_rows == 0) return ok();
+  if (!lse || !grad_logits) return fail(BI_ERR_NULL, "%s: lse and grad_logits are required", fn);
+  if (!aligned(lse, 4) || !aligned(token_weights, 4) || !aligned(grad_logits, 2))
+    return fail(BI_ERR_ALIGN, "%s: misaligned pointer", fn);
+  a.lse = lse;
+  a.token_weights = token_weights;
+  a.gout = static_cast<uint16_t*>(grad_logits);
+  a.ldg = grad_stride;
+  return lm_launch<true>(fn, a, stream);
 }
 
 }  // extern "C"

@@ -284,6 +284,55 @@ BI_API int64_t bi_lmhead_tiles(int64_t n_vocab_rows);
 /* lm_head rows per statistics tile of bi_lmhead_tile_stats (256). */
 BI_API int64_t bi_lmhead_tile_rows(void);
 
+/* Gradient of the lm_head logits: G[v, n] = w_n * (softmax(z_n)[v] - [v == y_n])
+ * for the rows of one vocabulary block, with z = hidden @ weight^T recomputed
+ * on the matrix cores by the same MFMA sequence as bi_lmhead_tile_stats and
+ * the lse from bi_stats_combine (the cross-entropy backward of PR #4685
+ * Summary, on the lm_head logits; bi_logprob_bwd's arithmetic per element).
+ *   lse            [n_tokens] fp32, the full-vocabulary lse of each token
+ *   token_weights  [n_tokens] fp32 or NULL (= 1); ignored tokens get +0.0,
+ *                  bad labels NaN (and BI_FLAG_BAD_LABEL)
+ *   grad_logits    [n_vocab_rows, grad_stride] bf16, vocabulary-major (row v
+ *                  holds the tokens), RNE; grad_stride >= n_tokens
+ *   other arguments as for bi_lmhead_tile_stats */
+BI_API int bi_lmhead_grad_logits(const void* hidden, const void* weight, int64_t n_tokens,
+                                 int64_t n_vocab_rows, int64_t d, int64_t hidden_stride,
+                                 int64_t weight_stride, int64_t vocab_offset, int64_t vocab,
+                                 const int64_t* labels, int64_t ignore_index, const float* lse,
+                                 const float* token_weights, void* grad_logits,
+                                 int64_t grad_stride, int32_t* status_flag, bi_stream_t stream);
+
+/* lm_head backward from the saved lse: grad_hidden += G @ weight and
+ * grad_weight = G^T @ hidden with G as in bi_lmhead_grad_logits (the chunked
+ * lm_head backward of "ZeroSyncGRPOTrainer - #6949": bf16 GEMMs with fp32
+ * accumulation).  The vocabulary block is processed in chunks of as many
+ * rows (a multiple of 256) as the workspace holds: per chunk the grad-logits
+ * kernel, then two rocBLAS GEMMs, all on `stream`.
+ *   grad_hidden    [n_tokens, grad_hidden_stride] fp32, ACCUMULATED (zero it
+ *                  for a fresh gradient; vocabulary shards add their parts)
+ *   grad_weight    [n_vocab_rows, grad_weight_stride] of grad_weight_dtype
+ *                  (BI_F32 or BI_BF16), overwritten
+ *   workspace      device memory, 256-byte aligned, of workspace_bytes >=
+ *                  bi_lmhead_backward_workspace(n_tokens, 256); it is in use
+ *                  until the queued work ends
+ * Sizes and strides must fit in 32 bits (the library GEMM's int).  The first
+ * call on a device creates the library's rocBLAS handle (which allocates);
+ * later calls allocate nothing.  Calls from several threads are serialized.
+ * n_tokens == 0 or n_vocab_rows == 0 writes nothing. */
+BI_API int bi_lmhead_backward(const void* hidden, const void* weight, int64_t n_tokens,
+                              int64_t n_vocab_rows, int64_t d, int64_t hidden_stride,
+                              int64_t weight_stride, int64_t vocab_offset, int64_t vocab,
+                              const int64_t* labels, int64_t ignore_index, const float* lse,
+                              const float* token_weights, float* grad_hidden,
+                              int64_t grad_hidden_stride, void* grad_weight,
+                              int grad_weight_dtype, int64_t grad_weight_stride,
+                              void* workspace, int64_t workspace_bytes, int32_t* status_flag,
+                              bi_stream_t stream);
+
+/* Workspace bytes for bi_lmhead_backward with chunks of chunk_rows lm_head
+ * rows (rounded up to a multiple of 256); -1 for bad arguments. */
+BI_API int64_t bi_lmhead_backward_workspace(int64_t n_tokens, int64_t chunk_rows);
+
 /* Human-readable name of a status code (static string). */
 BI_API const char* bi_status_string(int status);
 

@@ -271,6 +271,21 @@ def lmhead_tile_stats(hidden, weight, labels, vocab_offset: int, vocab: int, til
                                  ignore_index) for a in range(0, vc, tile)])
 
 
+def lmhead_backward(hidden, weight, labels, lse, token_weights=None,
+                    ignore_index: int = IGNORE_INDEX):
+    """(G [n, V], grad_hidden [n, d], grad_weight [V, d]) in float64.
+
+    G = w * (softmax - onehot) of the logits hidden @ weight^T from the given
+    lse (the cross-entropy backward, as `backward`); the chain rule through the
+    projection gives grad_hidden = G @ weight and grad_weight = G^T @ hidden
+    (the chunked lm_head backward of "ZeroSyncGRPOTrainer", exact here).
+    """
+    h = np.asarray(hidden, dtype=np.float64)
+    w = np.asarray(weight, dtype=np.float64)
+    g = backward(lmhead_logits(h, w), labels, lse, token_weights, ignore_index)
+    return g, g @ w, g.T @ h
+
+
 # ---------------------------------------------------------------------------
 # several label columns per row, and trainer-vs-generator difference metrics
 # ("[RL] Avoid full-vocab gather ...", Correctness and compatibility: the

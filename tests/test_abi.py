@@ -37,7 +37,8 @@ def test_header_declares_the_four_entry_points():
     for fn in ("bi_logprob_fwd", "bi_logprob_bwd", "bi_vocab_chunk_stats", "bi_stats_combine",
                "bi_logprob_fwd_bwd", "bi_policy_loss_fwd_bwd", "bi_logprob_fwd_multi",
                "bi_logprob_diff_stats", "bi_lmhead_tile_stats", "bi_lmhead_tiles",
-               "bi_lmhead_tile_rows"):
+               "bi_lmhead_tile_rows", "bi_lmhead_grad_logits", "bi_lmhead_backward",
+               "bi_lmhead_backward_workspace"):
         assert fn in names
 
 
@@ -162,6 +163,50 @@ def test_lmhead_argument_errors(L):
     assert t == 256
     assert L.bi_lmhead_tiles(300) == 2 and L.bi_lmhead_tiles(t) == 1 and L.bi_lmhead_tiles(0) == 0
     assert L.bi_lmhead_tiles(t + 1) == 2
+
+
+def test_lmhead_grad_logits_argument_errors(L):
+    f = L.bi_lmhead_grad_logits
+    args = dict(h=P, w=P, n=8, vc=300, d=128, ldh=128, ldw=128, off=0, v=300, lab=P, lse=P,
+                g=P, ldg=8)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["h"], a["w"], a["n"], a["vc"], a["d"], a["ldh"], a["ldw"], a["off"], a["v"],
+                 a["lab"], -100, a["lse"], NUL, a["g"], a["ldg"], NUL, NUL)
+
+    assert call(d=100) == bi.BI_ERR_SHAPE
+    assert call(ldg=7) == bi.BI_ERR_SHAPE          # grad stride below n_tokens
+    assert call(lse=NUL) == bi.BI_ERR_NULL
+    assert call(g=NUL) == bi.BI_ERR_NULL
+    assert call(g=ctypes.c_void_p(0x10001)) == bi.BI_ERR_ALIGN
+    assert call(n=0, h=NUL, w=NUL, lab=NUL, lse=NUL, g=NUL, ldg=0) == bi.BI_OK
+
+
+def test_lmhead_backward_argument_errors(L):
+    f = L.bi_lmhead_backward
+    ws = L.bi_lmhead_backward_workspace
+    need = ws(8, 256)
+    assert need == (32 << 20) + 256 * 8 * 2 and ws(9, 1) == (32 << 20) + 256 * 16 * 2
+    assert ws(-1, 256) == -1 and ws(8, 0) == -1
+    args = dict(h=P, w=P, n=8, vc=300, d=128, ldh=128, ldw=128, off=0, v=300, lab=P, lse=P,
+                gh=P, ldgh=128, gw=P, gdt=bi.BI_BF16, ldgw=128, ws=ctypes.c_void_p(0x100000),
+                wsb=need)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["h"], a["w"], a["n"], a["vc"], a["d"], a["ldh"], a["ldw"], a["off"], a["v"],
+                 a["lab"], -100, a["lse"], NUL, a["gh"], a["ldgh"], a["gw"], a["gdt"], a["ldgw"],
+                 a["ws"], a["wsb"], NUL, NUL)
+
+    assert call(gdt=7) == bi.BI_ERR_DTYPE
+    assert call(ldgh=100) == bi.BI_ERR_SHAPE       # gradient stride below d
+    assert call(n=1 << 31) == bi.BI_ERR_SHAPE      # beyond the library GEMM's 32-bit sizes
+    assert call(ws=NUL) == bi.BI_ERR_NULL
+    assert call(gh=NUL) == bi.BI_ERR_NULL
+    assert call(ws=ctypes.c_void_p(0x100010)) == bi.BI_ERR_ALIGN
+    assert call(wsb=need - 1) == bi.BI_ERR_SHAPE   # not even one 256-row chunk fits
+    assert call(n=0) == bi.BI_OK
 
 
 def chunk(L, logits=P, dtype=bi.BI_BF16, n=4, w=25, rs=100, off=25, v=100, labels=P,

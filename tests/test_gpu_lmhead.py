@@ -16,7 +16,7 @@ import torch
 import entropy_bi_logprob_amd as bi
 import oracle.bi_oracle as orc
 import workloads as wl
-from gpu_util import assert_close, dev, host
+from gpu_util import assert_close, dev, host, ulp_bf16
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-4
@@ -102,3 +102,115 @@ def test_qwen3_vocab_sampled_tokens():
     assert_close(host(lp)[rows], olp, TOL, "logprob")
     assert_close(host(ent)[rows], oent, TOL, "entropy")
     assert_close(host(lse)[rows], olse, TOL, "lse")
+
+
+# ---- backward: the gradient of the logits, and the two GEMMs
+
+def _setup(n, vc, d, seed, ignore_frac=0.1):
+    b = wl.lmhead_batch(n, vc, d, seed=seed, ignore_frac=ignore_frac)
+    H, W, labels = to_dev_bf16(b.hidden), to_dev_bf16(b.weight), dev(b.labels)
+    h = orc.decode(b.hidden, "bf16")
+    w = orc.decode(b.weight, "bf16")
+    _, _, olse = orc.forward(orc.lmhead_logits(h, w), b.labels)
+    tw = np.random.default_rng([seed, 9]).uniform(-1.5, 1.5, n).astype(np.float32)
+    return b, H, W, labels, h, w, olse, tw
+
+
+@pytest.mark.parametrize("n,vc,d", [(300, 1000, 128), (77, 333, 256), (513, 257, 192),
+                                    (5, 130, 64)])
+def test_grad_logits_against_oracle(n, vc, d):
+    b, H, W, labels, h, w, olse, tw = _setup(n, vc, d, seed=n + vc)
+    # the lse as the forward path produces it
+    _, _, lse = bi.lmhead_logprob(H, W, labels)
+    g = bi.lmhead_grad_logits(H, W, labels, lse, dev(tw))
+    torch.cuda.synchronize()
+    G, _, _ = orc.lmhead_backward(h, w, b.labels, host(lse), tw)
+    got = orc.decode(host(g.view(torch.int16)).view(np.uint16), "bf16").T   # [n, vc]
+    # fp32 logits and lse: |dp| <~ 1e-5 p; then one bf16 rounding (at most one
+    # ulp of the exact value, whichever binade the computed value falls in)
+    bound = 1e-5 * np.abs(tw)[:, None] + ulp_bf16(G)
+    assert np.all(np.abs(got - G) <= bound), float(np.max(np.abs(got - G) - bound))
+    ign = b.labels == -100
+    assert np.all(got[ign] == 0) and not np.any(np.signbit(got[ign]))
+
+
+def test_grad_logits_bad_label_is_nan_and_flagged():
+    b, H, W, labels, h, w, olse, tw = _setup(8, 300, 64, seed=4, ignore_frac=0.0)
+    lab = b.labels.copy()
+    lab[3] = 300 + 7
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    g = bi.lmhead_grad_logits(H, W, dev(lab), dev(olse.astype(np.float32)), status=flag)
+    torch.cuda.synchronize()
+    gf = host(g.float())
+    assert int(flag.item()) == bi.BI_FLAG_BAD_LABEL
+    assert np.isnan(gf[:, 3]).all() and np.isfinite(np.delete(gf, 3, axis=1)).all()
+
+
+def _check_grads(gh, gw, G, h, w, gw_bf16):
+    """|error| within bf16 rounding of G (2^-9 relative) plus fp32 accumulation,
+    bounded through the absolute products: (2^-8 + K 2^-24) |G| @ |operand|."""
+    _, oh, ow = G
+    Gm = G[0]
+    kv, kn = Gm.shape[1], Gm.shape[0]
+    bh = (2.0 ** -8 + kv * 2.0 ** -24) * (np.abs(Gm) @ np.abs(w)) + 1e-7
+    bw = (2.0 ** -8 + kn * 2.0 ** -24) * (np.abs(Gm).T @ np.abs(h)) + 1e-7
+    if gw_bf16:
+        bw = bw + 0.5 * ulp_bf16(ow)
+    eh, ew = np.abs(gh - oh), np.abs(gw - ow)
+    assert np.all(eh <= bh), float(np.max(eh - bh))
+    assert np.all(ew <= bw), float(np.max(ew - bw))
+
+
+@pytest.mark.parametrize("n,vc,d,chunk", [(300, 1000, 128, 256), (77, 333, 256, 16384),
+                                          (513, 1030, 192, 512), (5, 130, 64, 256)])
+@pytest.mark.parametrize("gdt", [torch.float32, torch.bfloat16], ids=["gw_f32", "gw_bf16"])
+def test_backward_against_oracle(n, vc, d, chunk, gdt):
+    b, H, W, labels, h, w, olse, tw = _setup(n, vc, d, seed=n + d)
+    _, _, lse = bi.lmhead_logprob(H, W, labels)
+    gh, gw = bi.lmhead_backward(H, W, labels, lse, dev(tw), grad_weight_dtype=gdt,
+                                chunk_rows=chunk)
+    torch.cuda.synchronize()
+    G = orc.lmhead_backward(h, w, b.labels, host(lse), tw)
+    _check_grads(host(gh), host(gw.float()), G, h, w, gdt == torch.bfloat16)
+
+
+def test_backward_accumulates_over_vocabulary_shards():
+    n, vc, d = 200, 1000, 128
+    b, H, W, labels, h, w, olse, tw = _setup(n, vc, d, seed=17)
+    _, _, lse = bi.lmhead_logprob(H, W, labels)
+    twd = dev(tw)
+    gh_full, gw_full = bi.lmhead_backward(H, W, labels, lse, twd, grad_weight_dtype=torch.float32)
+    # two shards (one split inside a 256-row tile) adding into one grad_hidden
+    gh = torch.zeros((n, d), dtype=torch.float32, device="cuda")
+    _, gwa = bi.lmhead_backward(H, W[:300].contiguous(), labels, lse, twd, 0, vc, grad_hidden=gh,
+                                grad_weight_dtype=torch.float32)
+    _, gwb = bi.lmhead_backward(H, W[300:].contiguous(), labels, lse, twd, 300, vc,
+                                grad_hidden=gh, grad_weight_dtype=torch.float32)
+    torch.cuda.synchronize()
+    G = orc.lmhead_backward(h, w, b.labels, host(lse), tw)
+    _check_grads(host(gh), host(torch.cat([gwa, gwb])), G, h, w, False)
+    _check_grads(host(gh_full), host(gw_full), G, h, w, False)
+
+
+def test_autograd_through_the_lm_head():
+    n, vc, d = 130, 700, 128
+    b, H, W, labels, h, w, olse, tw = _setup(n, vc, d, seed=23)
+    Hp = H.clone().requires_grad_(True)
+    Wp = W.clone().requires_grad_(True)
+    lp, ent = bi.lmhead_logprob_entropy(Hp, Wp, labels)
+    coef = torch.from_numpy(tw).cuda()
+    (lp * coef).sum().backward()
+    torch.cuda.synchronize()
+    # d(sum c lp)/dz = c (onehot - p): the backward with token weights -c
+    G = orc.lmhead_backward(h, w, b.labels, olse, -tw)
+    # the hidden gradient comes back in bf16 (the hidden dtype)
+    gh = host(Hp.grad.float())
+    gw = host(Wp.grad.float())
+    _, oh, ow = G
+    bh = (2.0 ** -8 + vc * 2.0 ** -24) * (np.abs(G[0]) @ np.abs(w)) + 0.5 * ulp_bf16(oh) + 1e-6
+    bw = (2.0 ** -8 + n * 2.0 ** -24) * (np.abs(G[0]).T @ np.abs(h)) + 0.5 * ulp_bf16(ow) + 1e-6
+    assert np.all(np.abs(gh - oh) <= bh) and np.all(np.abs(gw - ow) <= bw)
+    olp, oent, _ = orc.forward(orc.lmhead_logits(h, w), b.labels)
+    assert_close(host(lp.detach()), olp, TOL, "logprob")
+    assert_close(host(ent), oent, TOL, "entropy")
+

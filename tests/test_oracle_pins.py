@@ -603,3 +603,95 @@ def test_lmhead_tile_stats_combine_to_the_full_row():
     lp, ent, lse = orc.combine(st, labels, 300)
     flp, fent, flse = orc.forward(orc.lmhead_logits(H, W), labels)
     np.testing.assert_allclose(np.stack([lp, ent, lse]), np.stack([flp, fent, flse]), atol=1e-12)
+
+
+# ---- lm_head backward: chain rule through the projection
+
+def _lm_loss(H, W, labels, w):
+    """sum_n w_n * (-logprob_n) of the lm_head logits (ignored tokens: 0)."""
+    lp, _, _ = orc.forward(orc.lmhead_logits(H, W), labels)
+    return float(np.sum(w * -lp))
+
+
+def _lmhead_backward_fd_check(fn):
+    g = np.random.default_rng(31)
+    n, V, d = 4, 9, 5
+    H = g.standard_normal((n, d))
+    W = g.standard_normal((V, d)) * 0.7
+    labels = np.array([3, 0, -100, 8])
+    w = np.array([0.5, -1.25, 2.0, 1.0])
+    _, _, lse = orc.forward(orc.lmhead_logits(H, W), labels)
+    _, gh, gw = fn(H, W, labels, lse, w)
+    eps = 1e-6
+    for X, G in ((H, gh), (W, gw)):
+        num = np.zeros_like(X)
+        for idx in np.ndindex(*X.shape):
+            keep = X[idx]
+            X[idx] = keep + eps
+            up = _lm_loss(H, W, labels, w)
+            X[idx] = keep - eps
+            dn = _lm_loss(H, W, labels, w)
+            X[idx] = keep
+            num[idx] = (up - dn) / (2 * eps)
+        np.testing.assert_allclose(G, num, rtol=1e-6, atol=1e-7)
+
+
+def test_lmhead_backward_is_the_finite_difference_gradient():
+    _lmhead_backward_fd_check(orc.lmhead_backward)
+
+
+def test_lmhead_backward_zero_projection_closed_form():
+    # W = 0: every logit is 0, softmax is uniform, so grad_hidden = 0 and
+    # grad_weight[v] = sum_n w_n (1/V - [v == y_n]) H[n]
+    g = np.random.default_rng(32)
+    n, V, d = 5, 6, 3
+    H = g.standard_normal((n, d))
+    W = np.zeros((V, d))
+    labels = np.array([1, 5, -100, 0, 1])
+    w = g.uniform(0.5, 2.0, n)
+    _, _, lse = orc.forward(orc.lmhead_logits(H, W), labels)
+    np.testing.assert_allclose(lse, np.log(V), rtol=0, atol=1e-15)
+    G, gh, gw = orc.lmhead_backward(H, W, labels, lse, w)
+    assert np.all(gh == 0)
+    want = np.zeros((V, d))
+    for i in range(n):
+        if labels[i] == -100:
+            continue
+        for v in range(V):
+            want[v] += w[i] * (1.0 / V - (v == labels[i])) * H[i]
+    np.testing.assert_allclose(gw, want, rtol=1e-13, atol=1e-14)
+
+
+def test_lmhead_backward_ignored_tokens_contribute_nothing():
+    g = np.random.default_rng(33)
+    H = g.standard_normal((5, 4))
+    W = g.standard_normal((7, 4))
+    labels = np.array([2, -100, 6, 0, -100])
+    _, _, lse = orc.forward(orc.lmhead_logits(H, W), labels)
+    _, gh, gw = orc.lmhead_backward(H, W, labels, lse)
+    keep = labels != -100
+    _, gh2, gw2 = orc.lmhead_backward(H[keep], W, labels[keep], lse[keep])
+    assert np.all(gh[~keep] == 0)
+    np.testing.assert_allclose(gh[keep], gh2, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(gw, gw2, rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("mistake", ["transposed_weight_grad", "no_onehot", "weight_dropped",
+                                     "sign"])
+def test_lmhead_backward_planted_mistakes_are_caught(mistake):
+    def wrong(H, W, labels, lse, w):
+        G, gh, gw = orc.lmhead_backward(H, W, labels, lse, w)
+        if mistake == "transposed_weight_grad":
+            gw = (G.T @ H)[::-1]
+        elif mistake == "no_onehot":
+            p = orc.softmax_from_lse(orc.lmhead_logits(H, W), lse)
+            G2 = np.where(np.asarray(labels)[:, None] == -100, 0.0, w[:, None] * p)
+            gh, gw = G2 @ W, G2.T @ H
+        elif mistake == "weight_dropped":
+            _, gh, gw = orc.lmhead_backward(H, W, labels, lse, None)
+        elif mistake == "sign":
+            gh = -gh
+        return G, gh, gw
+    with pytest.raises(AssertionError):
+        _lmhead_backward_fd_check(wrong)
+
