@@ -425,7 +425,7 @@ def lmhead_backward(hidden: torch.Tensor, weight: torch.Tensor, labels: torch.Te
                     vocab_offset: int = 0, vocab: Optional[int] = None,
                     ignore_index: int = IGNORE_INDEX, *, grad_hidden: Optional[torch.Tensor] = None,
                     grad_weight: Optional[torch.Tensor] = None,
-                    grad_weight_dtype: torch.dtype = torch.bfloat16, chunk_rows: int = 16384,
+                    grad_weight_dtype: torch.dtype = torch.bfloat16, chunk_rows: int = 32768,
                     workspace: Optional[torch.Tensor] = None,
                     status: Optional[torch.Tensor] = None, stream=None):
     """(grad_hidden fp32 [N, d], grad_weight [Vc, d]) of sum_n w_n * CE_n through the
@@ -500,7 +500,7 @@ class LmHeadLogprobEntropy(torch.autograd.Function):
     lm_head logits hidden @ weight^T, which are never materialised."""
 
     @staticmethod
-    def forward(ctx, hidden, weight, labels, ignore_index=IGNORE_INDEX, chunk_rows=16384):
+    def forward(ctx, hidden, weight, labels, ignore_index=IGNORE_INDEX, chunk_rows=32768):
         lp, ent, lse = lmhead_logprob(hidden, weight, labels, ignore_index)
         ctx.save_for_backward(hidden, weight, labels, lse)
         ctx.ignore_index = ignore_index
@@ -517,6 +517,6 @@ class LmHeadLogprobEntropy(torch.autograd.Function):
         return gh.to(hidden.dtype), gw, None, None, None
 
 
-def lmhead_logprob_entropy(hidden, weight, labels, ignore_index=IGNORE_INDEX, chunk_rows=16384):
+def lmhead_logprob_entropy(hidden, weight, labels, ignore_index=IGNORE_INDEX, chunk_rows=32768):
     """Autograd-aware (logprob, entropy) straight from hidden states and lm_head rows."""
     return LmHeadLogprobEntropy.apply(hidden, weight, labels, ignore_index, chunk_rows)

@@ -3,7 +3,7 @@
     python -m entropy_bi_logprob_amd.build
 
 The library is a plain C ABI (include/bi_logprob.h) around hand-written HIP
-kernels; it links the HIP runtime and rocBLAS (the lm_head backward's two
+kernels; it links the HIP runtime and hipBLASLt (the lm_head backward's two
 plain GEMMs).
 """
 from __future__ import annotations
@@ -17,8 +17,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SOURCES = [os.path.join(PKG, "csrc", f)
            for f in ("bi_logprob.hip", "bi_lmhead.hip", "bi_lmhead_bwd.hip")]
-# the lm_head backward's two plain GEMMs are rocBLAS calls
-LIBS = ["-L/opt/rocm/lib", "-lrocblas"]
+# the lm_head backward's two plain GEMMs are hipBLASLt calls
+LIBS = ["-L/opt/rocm/lib", "-lhipblaslt"]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libbi_logprob.so")
 ARCH = "gfx950"

@@ -354,10 +354,16 @@ void lmhead_kernel(LmArgs p) {
   if constexpr (GRAD) {
     // gradient of the logits: w * (p - [v == y]), p = 2^((z - lse) * log2e)
     // as the row backward computes it; +0 for ignored tokens, NaN for bad
-    // labels.  Vocabulary-major bf16: lanes write consecutive tokens.
+    // labels.  The tile goes through LDS (the ring is free now) as bf16
+    // [vocab row][token], 16-byte chunks of a row XOR-swizzled by the row, so
+    // that it leaves as whole 16-byte vectors of 8 tokens: vocabulary-major.
+    static_assert(kTV * kTN * 2 <= kRing * kStageBytes, "grad tile fits the ring");
+    constexpr int kTileRowBytes = kTN * 2;
+    lds_barrier();   // every wave is done reading the ring
 #pragma unroll
     for (int y = 0; y < kYB; ++y) {
-      const int64_t j = n0 + kWN * wt + 32 * y + lr;
+      const int tok = kWN * wt + 32 * y + lr;   // token within the tile
+      const int64_t j = n0 + tok;
       if (j >= p.n_tok) continue;
       const int64_t lb = lab[y];
       const bool ignored = lb == p.ignore_index;
@@ -369,22 +375,42 @@ void lmhead_kernel(LmArgs p) {
       for (int x = 0; x < kXB; ++x)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int64_t i = wrow0 + 32 * x + 8 * (r >> 2) + 4 * half + (r & 3);
-          if (i < p.n_voc) {
-            float g;
-            if (ignored) {
-              g = 0.0f;
-            } else if (bad) {
-              g = NAN;
-            } else {
-              const float pr = exp2_hw((acc[x][y][r] - lse) * kLog2e);
-              g = i == yl ? w * (pr - 1.0f) : w * pr;
-            }
-            reinterpret_cast<__bf16*>(p.gout)[i * p.ldg + j] = __bf16(g);
+          const int row = kWV * wv + 32 * x + 8 * (r >> 2) + 4 * half + (r & 3);
+          float g;
+          if (ignored) {
+            g = 0.0f;
+          } else if (bad) {
+            g = NAN;
+          } else {
+            const float pr = exp2_hw((acc[x][y][r] - lse) * kLog2e);
+            g = v0 + row == yl ? w * (pr - 1.0f) : w * pr;
           }
+          const int at = row * kTileRowBytes + ((((tok >> 3) ^ (row & 31)) << 4) | ((tok & 7) << 1));
+          *reinterpret_cast<__bf16*>(ring + at) = __bf16(g);
         }
       if (bad && p.status_flag && tv == 0 && wv == 0 && half == 0)
         atomicOr(p.status_flag, BI_FLAG_BAD_LABEL);
+    }
+    wait_counts<63, 0>();
+    lds_barrier();
+    // rows v0 .. v0+255, 16-byte chunks of 8 tokens; 32 threads per row
+    const bool vec = (p.ldg % 8) == 0 && (reinterpret_cast<uintptr_t>(p.gout) % 16) == 0;
+    constexpr int kChunksPerRow = kTN / 8;
+#pragma unroll 4
+    for (int q = tid; q < kTV * kChunksPerRow; q += kThreads) {
+      const int row = q / kChunksPerRow, c = q % kChunksPerRow;
+      const int64_t i = v0 + row, j0 = n0 + 8 * c;
+      if (i >= p.n_voc || j0 >= p.n_tok) continue;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(
+          ring + row * kTileRowBytes + ((c ^ (row & 31)) << 4));
+      uint16_t* dst = p.gout + i * p.ldg + j0;
+      if (vec && j0 + 8 <= p.n_tok) {
+        *reinterpret_cast<u32x4*>(dst) = v;
+      } else {
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+        for (int e = 0; e < 8 && j0 + e < p.n_tok; ++e)
+          dst[e] = uint16_t(w4[e >> 1] >> (16 * (e & 1)));
+      }
     }
     return;
   }

@@ -14,16 +14,20 @@
 // workspace.  For each chunk, bi_lmhead_grad_logits recomputes its logits on
 // the matrix cores (the forward's exact MFMA sequence) and writes G for the
 // chunk as bf16, vocabulary-major [rows][n_tokens]; then two plain library
-// GEMMs (rocBLAS, bf16 operands, fp32 accumulation) add G @ W_chunk into
+// GEMMs (hipBLASLt, bf16 operands, fp32 accumulation) add G @ W_chunk into
 // grad_hidden and write G^T @ hidden into the chunk's grad_weight rows.  All
-// of it is queued on the caller's stream; rocBLAS works in the first part of
-// the caller's workspace, so nothing here allocates device memory except the
-// per-device rocBLAS handle, created on the first call on a device.
+// of it is queued on the caller's stream; hipBLASLt works in the first part
+// of the caller's workspace, so nothing here allocates device memory except
+// the per-device hipBLASLt handle, created on the first call on a device.
+// The algorithm of each GEMM shape is chosen once by hipBLASLt's heuristic
+// and kept, so a shape always runs the same kernel (reproducible results).
 
 #include <hip/hip_runtime.h>
-#include <rocblas/rocblas.h>
+#include <hipblaslt/hipblaslt.h>
 
+#include <map>
 #include <mutex>
+#include <tuple>
 
 #include "bi_common.h"
 
@@ -31,7 +35,7 @@ namespace {
 
 using namespace bi_internal;
 
-constexpr int64_t kBlasWorkspace = int64_t(32) << 20;   // rocBLAS's part of the workspace
+constexpr int64_t kBlasWorkspace = int64_t(128) << 20;  // hipBLASLt's part of the workspace
 constexpr int64_t kChunkAlign = 256;                    // lm_head rows per statistics tile
 constexpr int kMaxDevices = 64;
 
@@ -39,29 +43,108 @@ constexpr int kMaxDevices = 64;
 int64_t grad_ld(int64_t n_tokens) { return (n_tokens + 7) / 8 * 8; }
 
 std::mutex g_blas_mutex;
-rocblas_handle g_blas[kMaxDevices];
+hipblasLtHandle_t g_lt[kMaxDevices];
 
-int blas_status(const char* fn, const char* what, rocblas_status st) {
-  if (st == rocblas_status_success) return BI_OK;
-  return fail(BI_ERR_LAUNCH, "%s: %s: %s", fn, what, rocblas_status_to_string(st));
+// column-major D = op(A) op(B) + beta C, bf16 A and B, fp32 accumulation
+struct Gemm {
+  hipblasOperation_t ta, tb;
+  int64_t m, n, k, lda, ldb, ldc;
+  hipDataType ct;   // type of C and D
+  auto key(int dev) const {
+    return std::make_tuple(dev, int(ta), int(tb), m, n, k, lda, ldb, ldc, int(ct));
+  }
+};
+
+std::map<std::tuple<int, int, int, int64_t, int64_t, int64_t, int64_t, int64_t, int64_t, int>,
+         hipblasLtMatmulAlgo_t>
+    g_algos;
+
+int lt_status(const char* fn, const char* what, hipblasStatus_t st) {
+  if (st == HIPBLAS_STATUS_SUCCESS) return BI_OK;
+  return fail(BI_ERR_LAUNCH, "%s: %s failed (hipblasStatus %d)", fn, what, int(st));
 }
 
-// The calling thread's current device's handle (caller holds g_blas_mutex).
-int blas_handle(const char* fn, rocblas_handle* out) {
+// The calling thread's current device and its handle (caller holds g_blas_mutex).
+int lt_handle(const char* fn, int* dev_out, hipblasLtHandle_t* out) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
     return fail(BI_ERR_LAUNCH, "%s: no current HIP device", fn);
-  if (!g_blas[dev]) {
-    rocblas_handle h = nullptr;
-    if (int r = blas_status(fn, "rocblas_create_handle", rocblas_create_handle(&h))) return r;
-    // deterministic GEMMs: no atomics-based reductions
-    if (int r = blas_status(fn, "rocblas_set_atomics_mode",
-                            rocblas_set_atomics_mode(h, rocblas_atomics_not_allowed)))
-      return r;
-    g_blas[dev] = h;
+  if (!g_lt[dev]) {
+    hipblasLtHandle_t h = nullptr;
+    if (int r = lt_status(fn, "hipblasLtCreate", hipblasLtCreate(&h))) return r;
+    g_lt[dev] = h;
   }
-  *out = g_blas[dev];
+  *dev_out = dev;
+  *out = g_lt[dev];
   return BI_OK;
+}
+
+// Descriptors of one GEMM (host objects, released by the destructor).
+struct GemmDesc {
+  hipblasLtMatmulDesc_t op = nullptr;
+  hipblasLtMatrixLayout_t a = nullptr, b = nullptr, c = nullptr;
+  ~GemmDesc() {
+    if (c) hipblasLtMatrixLayoutDestroy(c);
+    if (b) hipblasLtMatrixLayoutDestroy(b);
+    if (a) hipblasLtMatrixLayoutDestroy(a);
+    if (op) hipblasLtMatmulDescDestroy(op);
+  }
+};
+
+int lt_gemm(const char* fn, hipblasLtHandle_t h, int dev, const Gemm& g, const void* A,
+            const void* B, float beta, void* C, void* ws, size_t ws_bytes, hipStream_t s) {
+  GemmDesc d;
+  const int32_t ta = g.ta, tb = g.tb;
+  if (int r = lt_status(fn, "matmul descriptor",
+                        hipblasLtMatmulDescCreate(&d.op, HIPBLAS_COMPUTE_32F, HIP_R_32F)))
+    return r;
+  if (int r = lt_status(fn, "transposes",
+                        hipblasLtMatmulDescSetAttribute(d.op, HIPBLASLT_MATMUL_DESC_TRANSA, &ta,
+                                                        sizeof(ta))))
+    return r;
+  if (int r = lt_status(fn, "transposes",
+                        hipblasLtMatmulDescSetAttribute(d.op, HIPBLASLT_MATMUL_DESC_TRANSB, &tb,
+                                                        sizeof(tb))))
+    return r;
+  const bool na = g.ta == HIPBLAS_OP_N, nb = g.tb == HIPBLAS_OP_N;
+  if (int r = lt_status(fn, "layouts",
+                        hipblasLtMatrixLayoutCreate(&d.a, HIP_R_16BF, na ? g.m : g.k,
+                                                    na ? g.k : g.m, g.lda)))
+    return r;
+  if (int r = lt_status(fn, "layouts",
+                        hipblasLtMatrixLayoutCreate(&d.b, HIP_R_16BF, nb ? g.k : g.n,
+                                                    nb ? g.n : g.k, g.ldb)))
+    return r;
+  if (int r = lt_status(fn, "layouts", hipblasLtMatrixLayoutCreate(&d.c, g.ct, g.m, g.n, g.ldc)))
+    return r;
+  auto it = g_algos.find(g.key(dev));
+  if (it == g_algos.end()) {
+    hipblasLtMatmulPreference_t pref = nullptr;
+    if (int r = lt_status(fn, "preference", hipblasLtMatmulPreferenceCreate(&pref))) return r;
+    const uint64_t max_ws = ws_bytes;
+    constexpr int kAsk = 8;
+    hipblasLtMatmulHeuristicResult_t res[kAsk];
+    int found = 0;
+    hipblasStatus_t st = hipblasLtMatmulPreferenceSetAttribute(
+        pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &max_ws, sizeof(max_ws));
+    if (st == HIPBLAS_STATUS_SUCCESS)
+      st = hipblasLtMatmulAlgoGetHeuristic(h, d.op, d.a, d.b, d.c, d.c, pref, kAsk, res, &found);
+    hipblasLtMatmulPreferenceDestroy(pref);
+    if (int r = lt_status(fn, "algorithm heuristic", st)) return r;
+    int pick = -1;   // the heuristic's first choice that fits the workspace
+    for (int i = 0; i < found && pick < 0; ++i)
+      if (res[i].state == HIPBLAS_STATUS_SUCCESS && res[i].workspaceSize <= ws_bytes) pick = i;
+    if (pick < 0)
+      return fail(BI_ERR_LAUNCH,
+                  "%s: no GEMM algorithm for %lld x %lld x %lld within %zu workspace bytes "
+                  "(%d candidates)", fn, (long long)g.m, (long long)g.n, (long long)g.k,
+                  ws_bytes, found);
+    it = g_algos.emplace(g.key(dev), res[pick].algo).first;
+  }
+  const float one = 1.0f;
+  return lt_status(fn, "hipblasLtMatmul",
+                   hipblasLtMatmul(h, d.op, &one, A, d.a, B, d.b, &beta, C, d.c, C, d.c,
+                                   &it->second, ws, ws_bytes, s));
 }
 
 }  // namespace
@@ -111,19 +194,13 @@ int bi_lmhead_backward(const void* hidden, const void* weight, int64_t n_tokens,
                 (long long)bi_lmhead_backward_workspace(n_tokens, kChunkAlign));
   uint16_t* g = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + kBlasWorkspace);
   const size_t gw_elem = grad_weight_dtype == BI_BF16 ? 2 : 4;
-  const rocblas_datatype gw_type =
-      grad_weight_dtype == BI_BF16 ? rocblas_datatype_bf16_r : rocblas_datatype_f32_r;
 
   std::lock_guard<std::mutex> lock(g_blas_mutex);
-  rocblas_handle h = nullptr;
-  if (int r = blas_handle(fn, &h)) return r;
-  if (int r = blas_status(fn, "rocblas_set_stream",
-                          rocblas_set_stream(h, static_cast<hipStream_t>(stream))))
-    return r;
-  if (int r = blas_status(fn, "rocblas_set_workspace",
-                          rocblas_set_workspace(h, workspace, size_t(kBlasWorkspace))))
-    return r;
-  const float one = 1.0f, zero = 0.0f;
+  int dev = -1;
+  hipblasLtHandle_t h = nullptr;
+  if (int r = lt_handle(fn, &dev, &h)) return r;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipDataType gw_type = grad_weight_dtype == BI_BF16 ? HIP_R_16BF : HIP_R_32F;
   for (int64_t c0 = 0; c0 < n_vocab_rows; c0 += chunk) {
     const int64_t rows = n_vocab_rows - c0 < chunk ? n_vocab_rows - c0 : chunk;
     const uint16_t* wc = static_cast<const uint16_t*>(weight) + c0 * weight_stride;
@@ -133,25 +210,17 @@ int bi_lmhead_backward(const void* hidden, const void* weight, int64_t n_tokens,
                                       stream))
       return r;
     // column-major view: grad_hidden^T (d x N) += W_c^T (d x rows) . (G^T: rows x N)
-    if (int r = blas_status(
-            fn, "rocblas_gemm_ex (grad_hidden)",
-            rocblas_gemm_ex(h, rocblas_operation_none, rocblas_operation_transpose, int(d),
-                            int(n_tokens), int(rows), &one, wc, rocblas_datatype_bf16_r,
-                            int(weight_stride), g, rocblas_datatype_bf16_r, int(ldg), &one,
-                            grad_hidden, rocblas_datatype_f32_r, int(grad_hidden_stride),
-                            grad_hidden, rocblas_datatype_f32_r, int(grad_hidden_stride),
-                            rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0)))
+    const Gemm dh{HIPBLAS_OP_N, HIPBLAS_OP_T, d, n_tokens, rows, weight_stride, ldg,
+                  grad_hidden_stride, HIP_R_32F};
+    if (int r = lt_gemm(fn, h, dev, dh, wc, g, 1.0f, grad_hidden, workspace,
+                        size_t(kBlasWorkspace), s))
       return r;
     // grad_weight_c^T (d x rows) = hidden^T (d x N) . G (N x rows)
     void* gwc = static_cast<char*>(grad_weight) + c0 * grad_weight_stride * int64_t(gw_elem);
-    if (int r = blas_status(
-            fn, "rocblas_gemm_ex (grad_weight)",
-            rocblas_gemm_ex(h, rocblas_operation_none, rocblas_operation_none, int(d), int(rows),
-                            int(n_tokens), &one, hidden, rocblas_datatype_bf16_r,
-                            int(hidden_stride), g, rocblas_datatype_bf16_r, int(ldg), &zero, gwc,
-                            gw_type, int(grad_weight_stride), gwc, gw_type,
-                            int(grad_weight_stride), rocblas_datatype_f32_r,
-                            rocblas_gemm_algo_standard, 0, 0)))
+    const Gemm dw{HIPBLAS_OP_N, HIPBLAS_OP_N, d, rows, n_tokens, hidden_stride, ldg,
+                  grad_weight_stride, gw_type};
+    if (int r = lt_gemm(fn, h, dev, dw, hidden, g, 0.0f, gwc, workspace, size_t(kBlasWorkspace),
+                        s))
       return r;
   }
   return launched(fn);

@@ -307,7 +307,8 @@ BI_API int bi_lmhead_grad_logits(const void* hidden, const void* weight, int64_t
  * lm_head backward of "ZeroSyncGRPOTrainer - #6949": bf16 GEMMs with fp32
  * accumulation).  The vocabulary block is processed in chunks of as many
  * rows (a multiple of 256) as the workspace holds: per chunk the grad-logits
- * kernel, then two rocBLAS GEMMs, all on `stream`.
+ * kernel, then two hipBLASLt GEMMs, all on `stream`; each GEMM shape keeps
+ * the algorithm chosen on its first call.
  *   grad_hidden    [n_tokens, grad_hidden_stride] fp32, ACCUMULATED (zero it
  *                  for a fresh gradient; vocabulary shards add their parts)
  *   grad_weight    [n_vocab_rows, grad_weight_stride] of grad_weight_dtype
@@ -315,8 +316,8 @@ BI_API int bi_lmhead_grad_logits(const void* hidden, const void* weight, int64_t
  *   workspace      device memory, 256-byte aligned, of workspace_bytes >=
  *                  bi_lmhead_backward_workspace(n_tokens, 256); it is in use
  *                  until the queued work ends
- * Sizes and strides must fit in 32 bits (the library GEMM's int).  The first
- * call on a device creates the library's rocBLAS handle (which allocates);
+ * Sizes and strides must fit in 32 bits.  The first call on a device creates
+ * the library's hipBLASLt handle (which allocates);
  * later calls allocate nothing.  Calls from several threads are serialized.
  * n_tokens == 0 or n_vocab_rows == 0 writes nothing. */
 BI_API int bi_lmhead_backward(const void* hidden, const void* weight, int64_t n_tokens,
