@@ -122,12 +122,40 @@ def lmhead_leg(bi, torch, np, wl, N, V, seed, steps, warm, stream):
 
     t_stats, t_comb = timed([lambda: bi.lmhead_tile_stats(H, W, labels, out=st, stream=stream),
                              lambda: bi.stats_combine(st, labels, out=outs, stream=stream)])
+    # backward from the saved lse (token weights: a mean over tokens)
+    lse = outs[2]
+    tw = torch.full((N,), -1.0 / N, dtype=torch.float32, device=dev)
+    gh = torch.zeros((N, d), dtype=torch.float32, device=dev)
+    gw = torch.empty((V, d), dtype=torch.bfloat16, device=dev)
+    chunk = 32768
+    ws = torch.empty(int(bi.lib().bi_lmhead_backward_workspace(N, chunk)), dtype=torch.uint8,
+                     device=dev)
+    (t_bwd,) = timed([lambda: bi.lmhead_backward(H, W, labels, lse, tw, grad_hidden=gh,
+                                                 grad_weight=gw, workspace=ws, stream=stream)])
+    del ws
     logits = torch.empty((N, V), dtype=torch.bfloat16, device=dev)
     t_gemm, t_fwd = timed([lambda: torch.matmul(H, W.t(), out=logits),
                            lambda: bi.fwd(logits, labels, out=outs, stream=stream)])
-    del logits, st
+    # unfused backward: logits, their gradient (10 GB each), then two library GEMMs
+    glog = torch.empty((N, V), dtype=torch.bfloat16, device=dev)
+    ghu = torch.empty((N, d), dtype=torch.bfloat16, device=dev)
+    t_ub = timed([lambda: torch.matmul(H, W.t(), out=logits),
+                  lambda: bi.bwd(logits, labels, lse, tw, torch.bfloat16, out=glog,
+                                 stream=stream),
+                  lambda: torch.matmul(glog, W, out=ghu),
+                  lambda: torch.matmul(glog.t(), H, out=gw)])
+    del logits, glog, st, ghu, gh, gw
+    # the pages' chunked-backward shape: 16 x 330 tokens, one tp = 4 vocabulary shard
+    ns, vs = 16 * 330, V // 4
+    Hs, Ws, ls = H[:ns].contiguous(), W[:vs].contiguous(), labels[:ns] % vs
+    _, _, lses = bi.lmhead_logprob(Hs, Ws, ls)
+    ghs = torch.zeros((ns, d), dtype=torch.float32, device=dev)
+    gws = torch.empty((vs, d), dtype=torch.bfloat16, device=dev)
+    (t_small,) = timed([lambda: bi.lmhead_backward(Hs, Ws, ls, lses, tw[:ns], grad_hidden=ghs,
+                                                   grad_weight=gws, stream=stream)])
     flops = 2.0 * N * V * d
     tf = flops / (t_stats * 1e-3) / 1e12
+    tfb = 3 * flops / (t_bwd * 1e-3) / 1e12
     return {"workload": f"hidden {N}x{d} bf16, lm_head {V}x{d} bf16",
             "fused_ms": t_stats + t_comb, "tile_stats_ms": t_stats, "combine_ms": t_comb,
             "rows_per_s": N / ((t_stats + t_comb) * 1e-3),
@@ -137,7 +165,21 @@ def lmhead_leg(bi, torch, np, wl, N, V, seed, steps, warm, stream):
                                      if (N, V, d) == (32768, 151936, 2560) else None)},
             "unfused_ms": t_gemm + t_fwd, "unfused_gemm_ms": t_gemm, "unfused_fwd_ms": t_fwd,
             "unfused_gemm_TFLOPs": flops / (t_gemm * 1e-3) / 1e12,
-            "speedup_vs_unfused": (t_gemm + t_fwd) / (t_stats + t_comb)}
+            "speedup_vs_unfused": (t_gemm + t_fwd) / (t_stats + t_comb),
+            "backward": {
+                "what": "bi_lmhead_backward: grad_hidden (fp32) and grad_weight (bf16) from the "
+                        "saved lse, 32768-row vocabulary chunks",
+                "ms": t_bwd, "TFLOPs_3gemm": tfb,
+                "roofline": {"bound": "mfma", "achieved": tfb, "peak": MFMA_BF16_PEAK_TFLOPS,
+                             "unit": "TFLOP/s", "frac": tfb / MFMA_BF16_PEAK_TFLOPS,
+                             "traffic": None},
+                "unfused_ms": sum(t_ub), "unfused_parts_ms": t_ub,
+                "unfused_what": "torch.matmul logits, bi_logprob_bwd to bf16, two torch.matmul "
+                                "(20 GB of logits and gradient)",
+                "speedup_vs_unfused": sum(t_ub) / t_bwd,
+                "pages_shape_ms": t_small,
+                "pages_shape": "16 x 330 tokens, 37984 vocabulary rows (one tp = 4 shard), "
+                               "d 2560"}}
 
 
 def cpu_baseline(rows_total, sample_rows, seed):
