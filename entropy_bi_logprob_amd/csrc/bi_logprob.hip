@@ -844,45 +844,50 @@ __global__ __launch_bounds__(kDiffThreads) void diff_stats_kernel(
   }
 }
 
-// Eight lanes per row: lane q takes chunks q, q+8, q+16, ... in ascending
-// order, then the eight partial sums are added by a fixed xor butterfly
-// (1, 2, 4), which leaves the same bits in every lane.  The order depends on
-// n_chunks only (batch-invariant).  Natural units throughout.
-constexpr int kCombineLanes = 8;
-constexpr int kCombineThreads = 256;
+// One thread per row, chunks in ascending order (natural units): the max
+// first (exact, any order), then the sums about it, chunk 0, 1, 2, ...  The
+// loads of eight chunks are issued ahead of their (in-order) arithmetic, and
+// workgroups are one wave, so that 32,768 rows occupy 512 workgroups.
+constexpr int kCombineThreads = 64;
+constexpr int kCombineAhead = 8;
 
-__device__ inline float xor_max(float v, int m) { return fmaxf(v, __shfl_xor(v, m, 64)); }
-__device__ inline float xor_add(float v, int m) { return v + __shfl_xor(v, m, 64); }
+__device__ inline void combine_step(const bi_stats& s, float M, float& S, float& U, float& t) {
+  t += s.target;
+  if (s.sumexp > 0.0f) {
+    const float gap = s.max - M;
+    const float a = exp2_hw(gap * kLog2e);
+    S = fmaf(a, s.sumexp, S);
+    U = fmaf(a, fmaf(gap, s.sumexp, s.sumexp_logit), U);
+  } else if (!(s.sumexp == 0.0f)) {   // NaN statistics propagate
+    S = NAN;
+  }
+}
 
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(
     const bi_stats* stats, int64_t n_chunks, int64_t n_rows, const int64_t* labels,
     int64_t ignore_index, float* logprob, float* entropy, float* lse_out) {
-  const int q = threadIdx.x % kCombineLanes;
-  const int64_t row = int64_t(blockIdx.x) * (kCombineThreads / kCombineLanes) +
-                      threadIdx.x / kCombineLanes;
-  const bool live = row < n_rows;   // dead lanes still take part in the shuffles
+  const int64_t row = int64_t(blockIdx.x) * kCombineThreads + threadIdx.x;
+  if (row >= n_rows) return;
+  const bi_stats* s = stats + row;   // chunk c at s[c * n_rows]
   float M = -INFINITY;
-  if (live)
-    for (int64_t c = q; c < n_chunks; c += kCombineLanes) M = fmaxf(M, stats[c * n_rows + row].max);
-  M = xor_max(xor_max(xor_max(M, 1), 2), 4);
+  int64_t c = 0;
+  for (; c + kCombineAhead <= n_chunks; c += kCombineAhead) {
+    float mx[kCombineAhead];
+#pragma unroll
+    for (int k = 0; k < kCombineAhead; ++k) mx[k] = s[(c + k) * n_rows].max;
+#pragma unroll
+    for (int k = 0; k < kCombineAhead; ++k) M = fmaxf(M, mx[k]);
+  }
+  for (; c < n_chunks; ++c) M = fmaxf(M, s[c * n_rows].max);
   float S = 0.0f, U = 0.0f, t = 0.0f;
-  if (live)
-    for (int64_t c = q; c < n_chunks; c += kCombineLanes) {
-      const bi_stats s = stats[c * n_rows + row];
-      t += s.target;
-      if (s.sumexp > 0.0f) {
-        const float gap = s.max - M;
-        const float a = exp2_hw(gap * kLog2e);
-        S = fmaf(a, s.sumexp, S);
-        U = fmaf(a, fmaf(gap, s.sumexp, s.sumexp_logit), U);
-      } else if (!(s.sumexp == 0.0f)) {   // NaN statistics propagate
-        S = NAN;
-      }
-    }
-  S = xor_add(xor_add(xor_add(S, 1), 2), 4);
-  U = xor_add(xor_add(xor_add(U, 1), 2), 4);
-  t = xor_add(xor_add(xor_add(t, 1), 2), 4);
-  if (!live || q != 0) return;
+  for (c = 0; c + kCombineAhead <= n_chunks; c += kCombineAhead) {
+    bi_stats v[kCombineAhead];
+#pragma unroll
+    for (int k = 0; k < kCombineAhead; ++k) v[k] = s[(c + k) * n_rows];
+#pragma unroll
+    for (int k = 0; k < kCombineAhead; ++k) combine_step(v[k], M, S, U, t);
+  }
+  for (; c < n_chunks; ++c) combine_step(s[c * n_rows], M, S, U, t);
   const float lnS = kLn2 * log2_hw(S);
   const float lse = S == 0.0f ? -INFINITY : M + lnS;
   const int64_t y = labels[row];
@@ -1218,8 +1223,7 @@ int bi_stats_combine(const bi_stats* stats, int64_t n_chunks, int64_t n_rows,
   if (!aligned(stats, 4) || !aligned(labels, 8) || !aligned(logprob, 4) || !aligned(entropy, 4) ||
       !aligned(lse, 4))
     return fail(BI_ERR_ALIGN, "%s: misaligned pointer", fn);
-  const int64_t rows_per_block = kCombineThreads / kCombineLanes;
-  const int64_t blocks = (n_rows + rows_per_block - 1) / rows_per_block;
+  const int64_t blocks = (n_rows + kCombineThreads - 1) / kCombineThreads;
   if (blocks > 0x7fffffff) return fail(BI_ERR_SHAPE, "%s: too many rows", fn);
   hipLaunchKernelGGL(combine_kernel, dim3(unsigned(blocks)), dim3(kCombineThreads), 0,
                      static_cast<hipStream_t>(stream), stats, n_chunks, n_rows, labels,

@@ -206,16 +206,12 @@ BI_API int bi_vocab_chunk_stats(const void* logits_chunk, int dtype, int64_t n_r
                          const int64_t* labels, int64_t ignore_index,
                          bi_stats* stats, int32_t* status_flag, bi_stream_t stream);
 
-/* Exact combine of chunk statistics.
+/* Exact combine of chunk statistics, chunks taken in ascending order.
  * Defined in PR #4685, Why, and the reply "Batch invariance under the
- * patched logprob path", Q2: M = max_c m_c is exact; then
- * S = sum_c e^(m_c - M) S_c, U = sum_c e^(m_c - M) (U_c + (m_c - M) S_c),
- * t = sum_c t_c; a chunk with S_c == 0 contributes nothing.  lse = M + ln S,
+ * patched logprob path", Q2: M = max_c m_c is exact; then, for c = 0, 1, ...,
+ * S += e^(m_c - M) S_c, U += e^(m_c - M) (U_c + (m_c - M) S_c), t += t_c;
+ * a chunk with S_c == 0 contributes nothing.  lse = M + ln S,
  * logprob = t - lse (+0.0 if ignored), entropy = ln S - U / S.
- * Summation order (fixed by n_chunks alone, hence batch-invariant): chunk c
- * goes to partial sum c mod 8, each partial sum takes its chunks in ascending
- * order, and the 8 partial sums are added pairwise by an xor butterfly
- * (partners at distance 1, then 2, then 4).
  *   stats    [n_chunks][n_rows] bi_stats (chunk-major)
  *   n_chunks >= 1
  *   logprob, entropy, lse  [n_rows] fp32 each; any may be NULL, not all
