@@ -90,7 +90,7 @@ def measured_traffic(kernel, summary=TRAFFIC_SUMMARY, sources=KERNEL_SOURCES):
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
 
 
-def lmhead_leg(bi, torch, np, wl, N, V, seed, steps, warm, stream):
+def lmhead_leg(bi, torch, np, wl, N, V, seed, steps, warm, stream, with_cpu=True):
     """Logprob/entropy straight from hidden states: hidden [N, 2560] x lm_head [V, 2560]^T
     on the matrix cores, reduced to statistics without materialising the logits; timed
     beside the unfused pipeline (library GEMM to bf16 logits, then bi_logprob_fwd)."""
@@ -156,6 +156,7 @@ def lmhead_leg(bi, torch, np, wl, N, V, seed, steps, warm, stream):
     flops = 2.0 * N * V * d
     tf = flops / (t_stats * 1e-3) / 1e12
     tfb = 3 * flops / (t_bwd * 1e-3) / 1e12
+    cpu = lmhead_cpu_baseline(b, np, wl) if with_cpu else None
     return {"workload": f"hidden {N}x{d} bf16, lm_head {V}x{d} bf16",
             "fused_ms": t_stats + t_comb, "tile_stats_ms": t_stats, "combine_ms": t_comb,
             "rows_per_s": N / ((t_stats + t_comb) * 1e-3),
@@ -179,7 +180,28 @@ def lmhead_leg(bi, torch, np, wl, N, V, seed, steps, warm, stream):
                 "speedup_vs_unfused": sum(t_ub) / t_bwd,
                 "pages_shape_ms": t_small,
                 "pages_shape": "16 x 330 tokens, 37984 vocabulary rows (one tp = 4 shard), "
-                               "d 2560"}}
+                               "d 2560"},
+            "cpu_baseline": cpu}
+
+
+def lmhead_cpu_baseline(b, np, wl, sample=256):
+    """The fp64 oracle on the first `sample` tokens of the lm_head workload: forward
+    (logits, logprob, entropy) and backward (the gradient of the logits, grad_hidden
+    and those tokens' grad_weight terms), full vocabulary and hidden size."""
+    import oracle.bi_oracle as orc
+
+    h = orc.decode(b.hidden[:sample], "bf16")
+    w = orc.decode(b.weight, "bf16")
+    labels = b.labels[:sample]
+    t0 = time.perf_counter()
+    lp, ent, lse = orc.forward(orc.lmhead_logits(h, w), labels)
+    t1 = time.perf_counter()
+    orc.lmhead_backward(h, w, labels, lse, np.full(sample, -1.0 / sample))
+    t2 = time.perf_counter()
+    return {"fwd_tokens_per_s": sample / (t1 - t0), "fwd_bwd_tokens_per_s": sample / (t2 - t0),
+            "unit": "tokens/s", "cores": wl.default_threads(), "kind": "oracle",
+            "sample": f"{sample} tokens x 151936 lm_head rows x d 2560, fp64 numpy "
+                      f"(BLAS threads as configured), {t2 - t0:.1f} s wall"}
 
 
 def cpu_baseline(rows_total, sample_rows, seed):
@@ -389,7 +411,8 @@ def main():
         "input_gen_s": gen_s,
     }
     if not args.no_lmhead:
-        line["lmhead"] = lmhead_leg(bi, torch, np, wl, N, V, seed, steps, warm, stream)
+        line["lmhead"] = lmhead_leg(bi, torch, np, wl, N, V, seed, steps, warm, stream,
+                                    with_cpu=not args.no_cpu_baseline and not args.profile_steps)
     if not args.no_cpu_baseline and not args.profile_steps:
         line["cpu_baseline"] = cpu_baseline(N, args.cpu_sample_rows, seed)
     print(json.dumps(line), flush=True)

@@ -119,16 +119,23 @@ struct LmArgs {
   int64_t ldg;
 };
 
-// Tile (tv, tn) of workgroup b; false for the padding workgroups of the grid.
+// Tile (tv, tn) of linear tile index t: groups of kGroup token tiles sweep
+// the vocabulary tiles together.
+__device__ inline void lm_tile_at(const LmArgs& p, int64_t t, int64_t* tv, int64_t* tn) {
+  const int64_t group = t / (kGroup * p.tiles_v), r = t % (kGroup * p.tiles_v);
+  const int64_t rows_in_group = min(int64_t(kGroup), p.tiles_n - group * kGroup);
+  *tn = group * kGroup + r % rows_in_group;
+  *tv = r / rows_in_group;
+}
+
+// Tile of workgroup b: workgroup b runs on XCD b % 8, and each XCD takes a
+// contiguous range of linear tile indices.  False for padding workgroups.
 __device__ inline bool lm_tile_of(const LmArgs& p, int64_t b, int64_t* tv, int64_t* tn) {
   const int64_t total = p.tiles_v * p.tiles_n;
   const int64_t per_xcd = (total + 7) / 8;
   const int64_t t = (b % 8) * per_xcd + b / 8;
   if (t >= total) return false;
-  const int64_t group = t / (kGroup * p.tiles_v), r = t % (kGroup * p.tiles_v);
-  const int64_t rows_in_group = min(int64_t(kGroup), p.tiles_n - group * kGroup);
-  *tn = group * kGroup + r % rows_in_group;
-  *tv = r / rows_in_group;
+  lm_tile_at(p, t, tv, tn);
   return true;
 }
 
@@ -158,29 +165,38 @@ typedef __attribute__((address_space(3))) void lds_void;
 // This lane's part of the direct-to-LDS fill: kLoads requests per stage,
 // each 16 bytes of global memory into 16 bytes of a 1 KB block that the wave
 // writes contiguously (lane order).  Block q of a stage holds kBlockRows
-// operand rows, of W for the first kLoadsW*4 blocks, then of H.
+// operand rows, of W for the first kLoadsW*kWaves blocks, then of H.  Request
+// i of this lane reads row row0 + kBlockRows*kWaves*i of its operand (W for
+// i < kLoadsW, else H), clamped to the tile's last valid row, at the chunk
+// that its LDS slot holds; the tile bases are uniform (SGPRs) and the lane's
+// offset is 32-bit.
 struct LmFill {
-  const char* src[kLoads];   // global address of this lane's chunk at k = 0
-  uint32_t lds[kLoads];      // wave-uniform LDS byte offset within a stage
+  const char* wbase;   // W row v0
+  const char* hbase;   // H row n0
+  uint32_t ldw2, ldh2; // row pitches in bytes
+  int wlast, hlast;    // last valid operand row within the tile
+  int row0;            // this lane's first row
+  uint32_t cbytes;     // byte offset of the chunk this lane's slot holds
+  uint32_t lds0;       // this wave's first block: wave * 1 KB
 };
 
 __device__ inline LmFill lm_fill_setup(const LmArgs& p, int64_t v0, int64_t n0, int wave,
                                        int lane) {
   LmFill f;
   const int rb = lane / kChunks, slot = lane % kChunks;
-#pragma unroll
-  for (int i = 0; i < kLoads; ++i) {
-    const int q = wave + kWaves * i;              // all blocks over the waves
-    const bool is_w = i < kLoadsW;                // a W block exactly when i < kLoadsW
-    const int r = kBlockRows * (is_w ? q : q - kLoadsW * kWaves) + rb;   // operand row
-    const int c = slot ^ lm_swz(r);               // global chunk stored in this slot
-    const int64_t row = is_w ? min(v0 + r, p.n_voc - 1) : min(n0 + r, p.n_tok - 1);
-    const uint16_t* base = is_w ? p.weight + row * p.ldw : p.hidden + row * p.ldh;
-    f.src[i] = reinterpret_cast<const char*>(base + 8 * c);
-    f.lds[i] = uint32_t(q) * 1024u;
-  }
+  f.row0 = kBlockRows * wave + rb;
+  f.cbytes = uint32_t(16 * (slot ^ lm_swz(f.row0)));   // lm_swz(row0 + 64 i) == lm_swz(row0)
+  f.wbase = reinterpret_cast<const char*>(p.weight + v0 * p.ldw);
+  f.hbase = reinterpret_cast<const char*>(p.hidden + n0 * p.ldh);
+  f.ldw2 = uint32_t(p.ldw * 2);
+  f.ldh2 = uint32_t(p.ldh * 2);
+  f.wlast = int(min(p.n_voc - v0, int64_t(kTV)) - 1);
+  f.hlast = int(min(p.n_tok - n0, int64_t(kTN)) - 1);
+  f.lds0 = uint32_t(wave) * 1024u;
   return f;
 }
+
+static_assert((kBlockRows * kWaves) % 32 == 0, "a lane's rows share one swizzle");
 
 // LDS byte address of a pointer into shared memory.
 __device__ inline uint32_t lds_addr(const char* p) {
@@ -195,9 +211,15 @@ __device__ inline uint32_t lds_addr(const char* p) {
 // The LDS-DMA load reads M0, which the compiler writes just before the asm
 // with a scalar instruction: one wait state (s_nop 0) must separate the two.
 __device__ inline void lm_fill1(const LmFill& f, uint32_t base, int stage, int i) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+  const bool is_w = i < kLoadsW;
+  const int step = kBlockRows * kWaves * (is_w ? i : i - kLoadsW);
+  const int row = min(f.row0 + step, is_w ? f.wlast : f.hlast);
+  const uint32_t off = uint32_t(row) * (is_w ? f.ldw2 : f.ldh2) + f.cbytes +
+                       uint32_t(stage) * kRowBytes;
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
-               : "v"(f.src[i] + stage * kRowBytes), "{m0}"(base + f.lds[i])
+               : "v"(off), "s"(is_w ? f.wbase : f.hbase),
+                 "{m0}"(base + f.lds0 + uint32_t(kWaves * i) * 1024u)
                : "memory");
 }
 
@@ -257,6 +279,92 @@ __device__ inline void lm_merge(Acc& a, float& ta, const Acc& b, float tb) {
   a.S = x.S + y.S;
   a.U = x.U + y.U;
   ta = ta + tb;
+}
+
+// Statistics of each token over one tile's 256 vocabulary rows, written as
+// the tile's bi_stats (fixed order: the lane's values, the lane halves, the
+// two vocabulary waves).
+__device__ inline void lm_stats_epilogue(const LmArgs& p, const f32x16 (&acc)[kXB][kYB],
+                                         const int64_t (&lab)[kYB], int64_t tv, int64_t tn,
+                                         int wv, int wt, int lr, int half,
+                                         float (&red)[kWT][kYB][32][4]) {
+  const int64_t v0 = tv * kTV, n0 = tn * kTN;
+  const int64_t wrow0 = v0 + kWV * wv;     // first vocabulary row of this wave
+  const bool full = v0 + kTV <= p.n_voc;   // uniform: no row of the tile is masked
+  float tl[kYB];
+  Acc lo[kYB];
+#pragma unroll
+  for (int y = 0; y < kYB; ++y) {
+    float z[16 * kXB];
+#pragma unroll
+    for (int x = 0; x < kXB; ++x)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t i = wrow0 + 32 * x + 8 * (r >> 2) + 4 * half + (r & 3);
+        z[16 * x + r] = (full || i < p.n_voc) ? acc[x][y][r] : -INFINITY;
+      }
+    Acc a = acc_empty();
+    accumulate<8, 2 * kXB>(a, z);
+    // the label's logit, held by exactly one lane of one vocabulary wave (if
+    // here); the select chain runs only when some lane of the wave needs it
+    float t = 0.0f;
+    const bool bad = lab[y] != p.ignore_index && (lab[y] < 0 || lab[y] >= p.vocab);
+    const int64_t yl = lab[y] - p.vocab_offset - wrow0;   // row within this wave's 128
+    const bool mine = !bad && lab[y] != p.ignore_index && lab[y] - p.vocab_offset < p.n_voc &&
+                      yl >= 0 && yl < kWV && half == ((yl >> 2) & 1);
+    if (__builtin_amdgcn_ballot_w64(mine)) {
+      const int q = int(yl >> 5) * 16 + int((yl & 31) >> 3) * 4 + int(yl & 3);
+#pragma unroll
+      for (int k = 0; k < 16 * kXB; ++k)
+        if (mine && q == k) t = z[k];
+    }
+    // lane halves (same token, other rows), lower half first
+    Acc o;
+    o.m = __shfl_xor(a.m, 32);
+    o.c = __shfl_xor(a.c, 32);
+    o.S = __shfl_xor(a.S, 32);
+    o.U = __shfl_xor(a.U, 32);
+    const float ot = __shfl_xor(t, 32);
+    Acc l = half ? o : a, h = half ? a : o;
+    float tlo = half ? ot : t, thi = half ? t : ot;
+    lm_merge(l, tlo, h, thi);
+    lo[y] = l;
+    tl[y] = tlo;
+    if (wv == 1 && half == 0) {
+      red[wt][y][lr][0] = l.m;
+      red[wt][y][lr][1] = l.S;
+      red[wt][y][lr][2] = l.U;
+      red[wt][y][lr][3] = tlo;
+    }
+  }
+  wait_counts<63, 0>();   // this wave's LDS writes are done
+  lds_barrier();
+  if (wv == 0 && half == 0) {
+#pragma unroll
+    for (int y = 0; y < kYB; ++y) {
+      const int64_t j = n0 + kWN * wt + 32 * y + lr;
+      Acc b;
+      b.m = red[wt][y][lr][0];
+      b.c = ref_of(b.m);
+      b.S = red[wt][y][lr][1];
+      b.U = red[wt][y][lr][2];
+      Acc a = lo[y];
+      float t = tl[y];
+      lm_merge(a, t, b, red[wt][y][lr][3]);
+      if (j < p.n_tok) {
+        const bool bad = lab[y] != p.ignore_index && (lab[y] < 0 || lab[y] >= p.vocab);
+        const float d = fmaf(a.m, kLog2e, a.c);
+        const float f = exp2_hw(-d);
+        bi_stats out;
+        out.max = a.m;
+        out.sumexp = a.S == 0.0f ? 0.0f : a.S * f;
+        out.sumexp_logit = a.S == 0.0f ? 0.0f : kLn2 * (fmaf(-d, a.S, a.U) * f);
+        out.target = bad ? NAN : t;
+        p.stats[tv * p.n_tok + j] = out;
+        if (bad && p.status_flag) atomicOr(p.status_flag, BI_FLAG_BAD_LABEL);
+      }
+    }
+  }
 }
 
 // GRAD = false: per-token statistics of each 256-row vocabulary tile.
@@ -415,81 +523,7 @@ void lmhead_kernel(LmArgs p) {
     return;
   }
 
-  // epilogue: statistics of each token over this tile's 256 vocabulary rows
-  const bool full = v0 + kTV <= p.n_voc;   // uniform: no row of the tile is masked
-  float tl[kYB];
-  Acc lo[kYB];
-#pragma unroll
-  for (int y = 0; y < kYB; ++y) {
-    float z[16 * kXB];
-#pragma unroll
-    for (int x = 0; x < kXB; ++x)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t i = wrow0 + 32 * x + 8 * (r >> 2) + 4 * half + (r & 3);
-        z[16 * x + r] = (full || i < p.n_voc) ? acc[x][y][r] : -INFINITY;
-      }
-    Acc a = acc_empty();
-    accumulate<8, 2 * kXB>(a, z);
-    // the label's logit, held by exactly one lane of one vocabulary wave (if
-    // here); the select chain runs only when some lane of the wave needs it
-    float t = 0.0f;
-    const bool bad = lab[y] != p.ignore_index && (lab[y] < 0 || lab[y] >= p.vocab);
-    const int64_t yl = lab[y] - p.vocab_offset - wrow0;   // row within this wave's 128
-    const bool mine = !bad && lab[y] != p.ignore_index && lab[y] - p.vocab_offset < p.n_voc &&
-                      yl >= 0 && yl < kWV && half == ((yl >> 2) & 1);
-    if (__builtin_amdgcn_ballot_w64(mine)) {
-      const int q = int(yl >> 5) * 16 + int((yl & 31) >> 3) * 4 + int(yl & 3);
-#pragma unroll
-      for (int k = 0; k < 16 * kXB; ++k)
-        if (mine && q == k) t = z[k];
-    }
-    // lane halves (same token, other rows), lower half first
-    Acc o;
-    o.m = __shfl_xor(a.m, 32);
-    o.c = __shfl_xor(a.c, 32);
-    o.S = __shfl_xor(a.S, 32);
-    o.U = __shfl_xor(a.U, 32);
-    const float ot = __shfl_xor(t, 32);
-    Acc l = half ? o : a, h = half ? a : o;
-    float tlo = half ? ot : t, thi = half ? t : ot;
-    lm_merge(l, tlo, h, thi);
-    lo[y] = l;
-    tl[y] = tlo;
-    if (wv == 1 && half == 0) {
-      red[wt][y][lr][0] = l.m;
-      red[wt][y][lr][1] = l.S;
-      red[wt][y][lr][2] = l.U;
-      red[wt][y][lr][3] = tlo;
-    }
-  }
-  __syncthreads();
-  if (wv == 0 && half == 0) {
-#pragma unroll
-    for (int y = 0; y < kYB; ++y) {
-      const int64_t j = n0 + kWN * wt + 32 * y + lr;
-      Acc b;
-      b.m = red[wt][y][lr][0];
-      b.c = ref_of(b.m);
-      b.S = red[wt][y][lr][1];
-      b.U = red[wt][y][lr][2];
-      Acc a = lo[y];
-      float t = tl[y];
-      lm_merge(a, t, b, red[wt][y][lr][3]);
-      if (j < p.n_tok) {
-        const bool bad = lab[y] != p.ignore_index && (lab[y] < 0 || lab[y] >= p.vocab);
-        const float d = fmaf(a.m, kLog2e, a.c);
-        const float f = exp2_hw(-d);
-        bi_stats out;
-        out.max = a.m;
-        out.sumexp = a.S == 0.0f ? 0.0f : a.S * f;
-        out.sumexp_logit = a.S == 0.0f ? 0.0f : kLn2 * (fmaf(-d, a.S, a.U) * f);
-        out.target = bad ? NAN : t;
-        p.stats[tv * p.n_tok + j] = out;
-        if (bad && p.status_flag) atomicOr(p.status_flag, BI_FLAG_BAD_LABEL);
-      }
-    }
-  }
+  lm_stats_epilogue(p, acc, lab, tv, tn, wv, wt, lr, half, red);
 }
 
 // Shared validation of the lm_head entry points; fills the common arguments.
@@ -498,11 +532,13 @@ int lm_setup(const char* fn, LmArgs* a, const void* hidden, const void* weight, 
              int64_t vocab_offset, int64_t vocab, const int64_t* labels, int64_t ignore_index,
              int32_t* status_flag) {
   if (n_tokens < 0 || n_vocab_rows < 0) return fail(BI_ERR_SHAPE, "%s: negative size", fn);
-  if (d < kBK || d % kBK != 0 || d > (int64_t(1) << 24))
-    return fail(BI_ERR_SHAPE, "%s: d = %lld must be a positive multiple of %d (at most 2^24)",
+  if (d < kBK || d % kBK != 0 || d > (int64_t(1) << 22))
+    return fail(BI_ERR_SHAPE, "%s: d = %lld must be a positive multiple of %d (at most 2^22)",
                 fn, (long long)d, kBK);
-  if (hidden_stride < d || weight_stride < d || hidden_stride % 8 || weight_stride % 8)
-    return fail(BI_ERR_SHAPE, "%s: strides must be >= d and multiples of 8 elements", fn);
+  if (hidden_stride < d || weight_stride < d || hidden_stride % 8 || weight_stride % 8 ||
+      hidden_stride > (int64_t(1) << 22) || weight_stride > (int64_t(1) << 22))
+    return fail(BI_ERR_SHAPE, "%s: strides must be >= d, multiples of 8 and at most 2^22 elements",
+                fn);
   if (vocab < 1 || vocab_offset < 0 || vocab_offset + n_vocab_rows > vocab)
     return fail(BI_ERR_SHAPE, "%s: rows [%lld, %lld) outside the vocabulary [0, %lld)", fn,
                 (long long)vocab_offset, (long long)(vocab_offset + n_vocab_rows),
@@ -533,10 +569,10 @@ int lm_setup(const char* fn, LmArgs* a, const void* hidden, const void* weight, 
 template <bool GRAD>
 int lm_launch(const char* fn, const LmArgs& a, bi_stream_t stream) {
   const int64_t total = a.tiles_v * a.tiles_n;
-  const int64_t blocks = 8 * ((total + 7) / 8);
+  int64_t blocks = 8 * ((total + 7) / 8);
   if (blocks > 0x7fffffff) return fail(BI_ERR_SHAPE, "%s: too many tiles", fn);
-  hipLaunchKernelGGL(lmhead_kernel<GRAD>, dim3(unsigned(blocks)), dim3(kThreads), 0,
-                     static_cast<hipStream_t>(stream), a);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(lmhead_kernel<GRAD>, dim3(unsigned(blocks)), dim3(kThreads), 0, s, a);
   return launched(fn);
 }
 

@@ -262,8 +262,8 @@ BI_API int bi_logprob_diff_stats(const float* a, const float* b, const int64_t* 
  *   hidden  [n_tokens, hidden_stride] bf16, 16-byte aligned rows
  *   weight  [n_vocab_rows, weight_stride] bf16 (the lm_head rows of global
  *           vocabulary ids vocab_offset .. vocab_offset + n_vocab_rows - 1)
- *   d       hidden size, a positive multiple of 64 (at most 2^24); strides
- *           multiples of 8
+ *   d       hidden size, a positive multiple of 64 (at most 2^22); strides
+ *           multiples of 8, at most 2^22 elements
  *   stats   [bi_lmhead_tiles(n_vocab_rows)][n_tokens] bi_stats, 16-byte aligned
  */
 BI_API int bi_lmhead_tile_stats(const void* hidden, const void* weight, int64_t n_tokens,

@@ -155,6 +155,9 @@ def test_lmhead_argument_errors(L):
     assert call(d=96) == bi.BI_ERR_SHAPE
     assert call(d=0) == bi.BI_ERR_SHAPE
     assert call(ldh=130) == bi.BI_ERR_SHAPE      # stride not a multiple of 8
+    assert call(ldw=(1 << 22) + 8) == bi.BI_ERR_SHAPE   # row pitch past 2^22 elements
+    assert call(d=1 << 22, ldh=1 << 22, ldw=(1 << 22) + 8) == bi.BI_ERR_SHAPE
+    assert call(d=(1 << 22) + 64, ldh=(1 << 22) + 64, ldw=(1 << 22) + 64) == bi.BI_ERR_SHAPE
     assert call(off=10) == bi.BI_ERR_SHAPE       # rows past the vocabulary
     assert call(h=NUL) == bi.BI_ERR_NULL
     assert call(w=ctypes.c_void_p(0x10008)) == bi.BI_ERR_ALIGN

@@ -56,6 +56,28 @@ def test_tiles_and_combine_against_oracle(n, vc, d):
     assert np.all(host(lp)[ign] == 0) and not np.any(np.signbit(host(lp)[ign]))
 
 
+@pytest.mark.parametrize("n,vc,d", [(1100, 20000, 128), (700, 30000, 64), (300, 60000, 192)])
+def test_many_tiles_per_workgroup(n, vc, d):
+    # more tiles than compute units: workgroups run several tiles in turn
+    # (K = 64 takes the one-tile-per-workgroup kernel); every tile is checked,
+    # and a token's tiles are bit-identical when it is computed alone
+    b = wl.lmhead_batch(n, vc, d, seed=n + d, ignore_frac=0.05)
+    H, W, labels = to_dev_bf16(b.hidden), to_dev_bf16(b.weight), dev(b.labels)
+    st = bi.lmhead_tile_stats(H, W, labels)
+    lp, ent, lse = bi.stats_combine(st, labels)
+    idx = torch.tensor([n - 1, 0, n // 2], device="cuda")
+    sub = bi.lmhead_tile_stats(H[idx].contiguous(), W, labels[idx].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(st[:, idx].contiguous().view(torch.int32), sub.view(torch.int32))
+    h = orc.decode(b.hidden, "bf16")
+    w = orc.decode(b.weight, "bf16")
+    check_tiles(host(st), orc.lmhead_tile_stats(h, w, b.labels, 0, vc, bi.lmhead_tile_rows()))
+    olp, oent, olse = orc.forward(orc.lmhead_logits(h, w), b.labels)
+    assert_close(host(lp), olp, TOL, "logprob")
+    assert_close(host(ent), oent, TOL, "entropy")
+    assert_close(host(lse), olse, TOL, "lse")
+
+
 def test_tiles_do_not_depend_on_the_batch():
     n, vc, d = 640, 1500, 256
     b = wl.lmhead_batch(n, vc, d, seed=3)
