@@ -43,6 +43,8 @@
 //    vocabulary tiles together, so concurrent tiles share W and H slices in
 //    that XCD's L2.
 
+#include <type_traits>
+
 #include "bi_common.h"
 
 namespace {
@@ -54,11 +56,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // Tuning knobs (shape of the pipeline only; every choice computes the same
 // statistics tile of 256 vocabulary rows, bit for bit).
-#ifndef BI_LM_TILE_N
-#define BI_LM_TILE_N 256   // tokens per tile: 256 (one workgroup per CU) or 128
-#endif
-#ifndef BI_LM_RING
-#define BI_LM_RING 2       // LDS stages in the ring
+#ifndef BI_LM_SLOTS
+#define BI_LM_SLOTS 4      // LDS slots of one operand's stage: 4 (two whole stages) or 5
 #endif
 #ifndef BI_LM_GROUP
 #define BI_LM_GROUP 8      // token tiles that sweep the vocabulary together
@@ -71,7 +70,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 #endif
 
 constexpr int kTV = 256;                  // vocab rows per tile (= per statistics tile)
-constexpr int kTN = BI_LM_TILE_N;         // tokens per tile
+constexpr int kTN = kTV;                  // tokens per tile
 constexpr int kWaves = BI_LM_WAVES;
 constexpr int kWT = kWaves / 2;           // token waves (vocab waves: 2)
 constexpr int kWV = kTV / 2;              // vocab rows per wave
@@ -82,26 +81,26 @@ constexpr int kBK = BI_LM_BK;             // K per LDS stage
 constexpr int kKS = kBK / 16;             // MFMA K steps per stage
 constexpr int kChunks = kBK / 8;          // 16-byte chunks per row slice
 constexpr int kBlockRows = 1024 / (kBK * 2);   // rows per 1 KB fill block
-constexpr int kRing = BI_LM_RING;         // LDS stages in the ring
+constexpr int kSlots = BI_LM_SLOTS;       // LDS slots, one operand's stage each
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRowBytes = kBK * 2;        // bytes per row per stage
-constexpr int kOpW = kTV * kRowBytes;     // W part of a stage
-constexpr int kStageBytes = (kTV + kTN) * kRowBytes;
-constexpr int kLoads = kStageBytes / (kThreads * 16);       // per lane per stage
-constexpr int kLoadsW = kOpW / (kThreads * 16);             // of which W
+constexpr int kUnitBytes = kTV * kRowBytes;   // one operand's rows of one stage
+constexpr int kRingBytes = kSlots * kUnitBytes;
+constexpr int kLoadsU = kUnitBytes / (kThreads * 16);       // requests per lane per unit
+constexpr int kLoads = 2 * kLoadsU;                         // per lane per stage
 constexpr int kGroup = BI_LM_GROUP;       // token tiles that sweep together
 
-static_assert(kStageBytes % (kThreads * 16) == 0 && kOpW % (kThreads * 16) == 0, "fill split");
-static_assert(kTN == 128 || kTN == 256, "tile shape");
+static_assert(kUnitBytes % (kThreads * 16) == 0, "fill split");
 static_assert(kBK == 32 || kBK == 64, "stage depth");
-static_assert(kRing >= 2 && (kRing - 1) * kLoads < 64, "ring depth");
-static_assert(kRing * kStageBytes + 8192 <= 160 * 1024, "LDS size");
+static_assert(kSlots >= 4 && (kSlots - 2) * kLoadsU < 64, "ring depth");
+static_assert(kRingBytes <= 160 * 1024, "LDS size");
 static_assert(kWaves == 4 || kWaves == 8, "waves");
 static_assert(kWN % 32 == 0, "wave tile");
 static_assert(kXB * kYB >= kXB + kYB, "one fragment read per MFMA");
-// workgroups that fit one CU's 160 KB of LDS, hence waves per SIMD
-constexpr int kWGsPerCU = (160 * 1024) / (kRing * kStageBytes + kWT * kYB * 32 * 16);
-constexpr int kWavesPerEU = (kWGsPerCU > 2 ? 2 : kWGsPerCU) * kWaves / 4;
+// waves per SIMD: eight-wave workgroups need ~210 registers a wave (two waves
+// a SIMD); four-wave ones run two workgroups a CU when the LDS allows
+constexpr int kWGsPerCU = (160 * 1024) / kRingBytes;
+constexpr int kWavesPerEU = kWaves == 8 ? 2 : (kWGsPerCU >= 2 ? 2 : 1);
 
 struct LmArgs {
   const uint16_t* hidden;   // [n_tok, ldh] bf16 bits
@@ -162,14 +161,16 @@ __device__ inline void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// This lane's part of the direct-to-LDS fill: kLoads requests per stage,
+// The K loop streams units: unit 2s holds stage s's 256 W rows (kBK wide),
+// unit 2s+1 its 256 H rows, and unit u lands in LDS slot u % kSlots.  With
+// four slots that is a ring of two whole stages; a fifth slot lets every
+// stage's W unit be requested a stage earlier, so 1.5 stages are in flight
+// instead of one.  This lane's part of filling one unit: kLoadsU requests,
 // each 16 bytes of global memory into 16 bytes of a 1 KB block that the wave
-// writes contiguously (lane order).  Block q of a stage holds kBlockRows
-// operand rows, of W for the first kLoadsW*kWaves blocks, then of H.  Request
-// i of this lane reads row row0 + kBlockRows*kWaves*i of its operand (W for
-// i < kLoadsW, else H), clamped to the tile's last valid row, at the chunk
-// that its LDS slot holds; the tile bases are uniform (SGPRs) and the lane's
-// offset is 32-bit.
+// writes contiguously (lane order); block q of the slot holds kBlockRows
+// rows.  Request i reads row row0 + kBlockRows*kWaves*i of the operand,
+// clamped to the tile's last valid row, at the chunk that its LDS position
+// holds; the tile bases are uniform (SGPRs) and the lane's offset is 32-bit.
 struct LmFill {
   const char* wbase;   // W row v0
   const char* hbase;   // H row n0
@@ -203,50 +204,65 @@ __device__ inline uint32_t lds_addr(const char* p) {
   return uint32_t(reinterpret_cast<uintptr_t>((const lds_void*)p));
 }
 
-// Request stage `stage` into the ring buffer `dst`.  Written as inline
+// Request i of one unit: operand W (is_w) or H, K stage `stage`, into the
+// slot at LDS address `slot`.  Written as inline
 // assembly so that the compiler does not track these LDS writes: it would
 // otherwise wait for every request in flight before any LDS read.  The waits
 // are explicit instead (wait_counts before each barrier); the compiler's own
 // vmcnt waits stay correct, since extra requests only make them stricter.
 // The LDS-DMA load reads M0, which the compiler writes just before the asm
 // with a scalar instruction: one wait state (s_nop 0) must separate the two.
-__device__ inline void lm_fill1(const LmFill& f, uint32_t base, int stage, int i) {
-  const bool is_w = i < kLoadsW;
-  const int step = kBlockRows * kWaves * (is_w ? i : i - kLoadsW);
-  const int row = min(f.row0 + step, is_w ? f.wlast : f.hlast);
+__device__ inline void lm_fill1(const LmFill& f, uint32_t slot, int stage, bool is_w, int i) {
+  const int row = min(f.row0 + kBlockRows * kWaves * i, is_w ? f.wlast : f.hlast);
   const uint32_t off = uint32_t(row) * (is_w ? f.ldw2 : f.ldh2) + f.cbytes +
                        uint32_t(stage) * kRowBytes;
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
                : "v"(off), "s"(is_w ? f.wbase : f.hbase),
-                 "{m0}"(base + f.lds0 + uint32_t(kWaves * i) * 1024u)
+                 "{m0}"(slot + f.lds0 + uint32_t(kWaves * i) * 1024u)
                : "memory");
 }
 
-__device__ inline void lm_fill(const LmFill& f, const char* dst, int stage) {
-#pragma unroll
-  for (int i = 0; i < kLoads; ++i) lm_fill1(f, lds_addr(dst), stage, i);
+// Request i of unit u (0 <= i < kLoadsU) into the ring at LDS address `ring`;
+// units past the last stage (u >= 2 ns) are not requested.
+__device__ inline void lm_fill_unit1(const LmFill& f, uint32_t ring, int u, int ns, int i) {
+  if ((u >> 1) < ns)
+    lm_fill1(f, ring + uint32_t(u % kSlots) * kUnitBytes, u >> 1, (u & 1) == 0, i);
+}
+
+// Wait until at most n of this wave's newest units are still in flight
+// (0 <= n <= kSlots - 2; requests complete in order) and its LDS reads are done.
+__device__ inline void wait_units(int n) {
+  static_assert(kSlots <= 5, "wait_units covers n <= 3");
+  switch (n) {
+    case 0: wait_counts<0, 0>(); break;
+    case 1: wait_counts<kLoadsU, 0>(); break;
+    case 2: wait_counts<2 * kLoadsU, 0>(); break;
+    default: wait_counts<3 * kLoadsU, 0>(); break;
+  }
 }
 
 struct LmFrag {
   bf16x8 a[kXB], b[kYB];
 };
 
-// Operand fragment j of one K step of the stage held in the ring buffer s,
-// in the order the step's MFMAs first use them (A0, B0 .. B(kYB-1), A1 ..).
-__device__ inline void lm_read1(LmFrag& fr, const char* s, uint32_t off_w, uint32_t off_h,
-                                int j) {
+// Operand fragment j of one K step of the stage whose W and H units are in
+// the slots w and h, in the order the step's MFMAs first use them (A0,
+// B0 .. B(kYB-1), A1 ..).
+__device__ inline void lm_read1(LmFrag& fr, const char* w, const char* h, uint32_t off_w,
+                                uint32_t off_h, int j) {
   if (j >= 1 && j <= kYB) {
-    fr.b[j - 1] = *reinterpret_cast<const bf16x8*>(s + off_h + (j - 1) * 32 * kRowBytes);
+    fr.b[j - 1] = *reinterpret_cast<const bf16x8*>(h + off_h + (j - 1) * 32 * kRowBytes);
   } else {
     const int x = j == 0 ? 0 : j - kYB;
-    fr.a[x] = *reinterpret_cast<const bf16x8*>(s + off_w + x * 32 * kRowBytes);
+    fr.a[x] = *reinterpret_cast<const bf16x8*>(w + off_w + x * 32 * kRowBytes);
   }
 }
 
-__device__ inline void lm_read(LmFrag& fr, const char* s, uint32_t off_w, uint32_t off_h) {
+__device__ inline void lm_read(LmFrag& fr, const char* w, const char* h, uint32_t off_w,
+                               uint32_t off_h) {
 #pragma unroll
-  for (int j = 0; j < kXB + kYB; ++j) lm_read1(fr, s, off_w, off_h, j);
+  for (int j = 0; j < kXB + kYB; ++j) lm_read1(fr, w, h, off_w, off_h, j);
 }
 
 constexpr int kMfmas = kXB * kYB;                      // MFMAs per wave per K step
@@ -290,7 +306,8 @@ __device__ inline void lm_stats_epilogue(const LmArgs& p, const f32x16 (&acc)[kX
                                          float (&red)[kWT][kYB][32][4]) {
   const int64_t v0 = tv * kTV, n0 = tn * kTN;
   const int64_t wrow0 = v0 + kWV * wv;     // first vocabulary row of this wave
-  const bool full = v0 + kTV <= p.n_voc;   // uniform: no row of the tile is masked
+  // rows of this wave that exist (uniform); the others are masked to -inf
+  const int valid = int(max(int64_t(0), min(p.n_voc - wrow0, int64_t(kWV))));
   float tl[kYB];
   Acc lo[kYB];
 #pragma unroll
@@ -300,8 +317,8 @@ __device__ inline void lm_stats_epilogue(const LmArgs& p, const f32x16 (&acc)[kX
     for (int x = 0; x < kXB; ++x)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t i = wrow0 + 32 * x + 8 * (r >> 2) + 4 * half + (r & 3);
-        z[16 * x + r] = (full || i < p.n_voc) ? acc[x][y][r] : -INFINITY;
+        const int row = 32 * x + 8 * (r >> 2) + 4 * half + (r & 3);   // within the wave
+        z[16 * x + r] = row < valid ? acc[x][y][r] : -INFINITY;
       }
     Acc a = acc_empty();
     accumulate<8, 2 * kXB>(a, z);
@@ -313,10 +330,9 @@ __device__ inline void lm_stats_epilogue(const LmArgs& p, const f32x16 (&acc)[kX
     const bool mine = !bad && lab[y] != p.ignore_index && lab[y] - p.vocab_offset < p.n_voc &&
                       yl >= 0 && yl < kWV && half == ((yl >> 2) & 1);
     if (__builtin_amdgcn_ballot_w64(mine)) {
-      const int q = int(yl >> 5) * 16 + int((yl & 31) >> 3) * 4 + int(yl & 3);
+      const int q = mine ? int(yl >> 5) * 16 + int((yl & 31) >> 3) * 4 + int(yl & 3) : -1;
 #pragma unroll
-      for (int k = 0; k < 16 * kXB; ++k)
-        if (mine && q == k) t = z[k];
+      for (int k = 0; k < 16 * kXB; ++k) t = q == k ? z[k] : t;
     }
     // lane halves (same token, other rows), lower half first
     Acc o;
@@ -374,8 +390,7 @@ __device__ inline void lm_stats_epilogue(const LmArgs& p, const f32x16 (&acc)[kX
 template <bool GRAD>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEU, kWavesPerEU)))
 void lmhead_kernel(LmArgs p) {
-  __shared__ __attribute__((aligned(1024))) char ring[kRing * kStageBytes];
-  __shared__ float red[kWT][kYB][32][4];
+  __shared__ __attribute__((aligned(1024))) char ring[kRingBytes];
   int64_t tv, tn;
   if (!lm_tile_of(p, blockIdx.x, &tv, &tn)) return;   // whole workgroup exits together
   const int tid = threadIdx.x, lane = tid & 63;
@@ -401,7 +416,7 @@ void lmhead_kernel(LmArgs p) {
   for (int kk = 0; kk < kKS; ++kk) {
     const uint32_t in_row = uint32_t(lr * kRowBytes + 16 * ((2 * kk + half) ^ lm_swz(lr)));
     off_w[kk] = uint32_t(kWV * wv * kRowBytes) + in_row;
-    off_h[kk] = uint32_t(kOpW + kWN * wt * kRowBytes) + in_row;
+    off_h[kk] = uint32_t(kWN * wt * kRowBytes) + in_row;
   }
 
   f32x16 acc[kXB][kYB];
@@ -412,51 +427,77 @@ void lmhead_kernel(LmArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[x][y][r] = 0.0f;
 
-  // prologue: stages 0 .. kRing-1 requested, stage 0 landed and visible.  Requests
-  // past the last stage re-read the last stage into a buffer nobody reads
-  // again, so every stage has the same kLoads requests per lane in flight.
+  // prologue: units 0 .. kSlots-1 requested, stage 0 (units 0 and 1) landed
+  // and visible
+  const uint32_t rbase = lds_addr(ring);
 #pragma unroll
-  for (int b = 0; b < kRing; ++b) lm_fill(fill, ring + b * kStageBytes, min(b, ns - 1));
-  wait_counts<(kRing - 1) * kLoads, 15>();
+  for (int u = 0; u < kSlots; ++u)
+#pragma unroll
+    for (int i = 0; i < kLoadsU; ++i) lm_fill_unit1(fill, rbase, u, ns, i);
+  wait_units(min(kSlots, 2 * ns) - 2);   // units 2 .. min(kSlots, 2 ns) - 1 may fly on
   lds_barrier();
   LmFrag fr[2];
-  lm_read(fr[0], ring, off_w[0], off_h[0]);
+  lm_read(fr[0], ring, ring + kUnitBytes, off_w[0], off_h[0]);
 
-  // Stage s from ring buffer `cur`, K step kk's fragments in fr[kk & 1]: the
-  // next step's fragments are read while this step's MFMAs run.  Before the
-  // last step's MFMAs: stage s+1 must have landed (this wave's requests; the
-  // barrier covers the other waves') and this wave's reads of stage s must be
-  // done; after the barrier stage s+1 is visible and stage s's buffer is free
-  // for stage s+kRing, whose requests are spread over the last step.
-  int cur = 0;
-  for (int s = 0; s < ns; ++s) {
-    const int nxt = cur == kRing - 1 ? 0 : cur + 1;
-    const char* cbuf = ring + cur * kStageBytes;
+  // Stage s from the slots of units 2s (W) and 2s+1 (H), K step kk's
+  // fragments in fr[kk & 1]: the next step's fragments are read while this
+  // step's MFMAs run.  Before the last step's MFMAs: stage s+1 must have
+  // landed (this wave's requests: all but the units requested after unit
+  // 2s+3, at most kSlots-4 of them; the barrier covers the other waves'),
+  // and this wave's reads of stage s must be done; after the barrier stage
+  // s+1 is visible and stage s's two slots are free for units 2s+kSlots and
+  // 2s+kSlots+1, whose requests are spread over the last step.  Those units
+  // exist (stage < ns) for every stage but the last kTail ones: the stages
+  // before them run without a branch (TAIL = false), the last ones check.
+  constexpr int kTail = (kSlots + 1) / 2;
+  int sw = 0;   // slot of stage s's W unit; its H unit is in the next slot
+  auto stage = [&](int s, auto tail) {
+    constexpr bool TAIL = decltype(tail)::value;
+    const int sh = sw + 1 == kSlots ? 0 : sw + 1;
+    const int nw = sh + 1 == kSlots ? 0 : sh + 1;   // stage s+1's slots
+    const int nh = nw + 1 == kSlots ? 0 : nw + 1;
+    const char* wbuf = ring + sw * kUnitBytes;
+    const char* hbuf = ring + sh * kUnitBytes;
 #pragma unroll
     for (int kk = 0; kk < kKS; ++kk) {
       LmFrag& now = fr[kk & 1];
       LmFrag& next = fr[(kk + 1) & 1];
       if (kk + 1 < kKS) {
         lm_mma_with(now, acc, [&](int m) {
-          if (m < kXB + kYB) lm_read1(next, cbuf, off_w[kk + 1], off_h[kk + 1], m);
+          if (m < kXB + kYB) lm_read1(next, wbuf, hbuf, off_w[kk + 1], off_h[kk + 1], m);
         });
       } else {
-        wait_counts<(kRing - 2) * kLoads, 0>();
+        // units requested so far: 0 .. min(2s + kSlots, 2ns) - 1
+        if (TAIL) wait_units(max(0, min(2 * s + kSlots, 2 * ns) - (2 * s + 4)));
+        else wait_counts<(kSlots - 4) * kLoadsU, 0>();
         lds_barrier();
-        const uint32_t fbase = lds_addr(cbuf);
-        const int fstage = min(s + kRing, ns - 1);
-        const char* nbuf = ring + nxt * kStageBytes;
+        // unit 2s+kSlots into slot sw, unit 2s+kSlots+1 into slot sh
+        const uint32_t fa = rbase + uint32_t(sw) * kUnitBytes;
+        const uint32_t fb = rbase + uint32_t(sh) * kUnitBytes;
+        const int sa = s + kSlots / 2, sb = s + (kSlots + 1) / 2;
+        const char* nwbuf = ring + nw * kUnitBytes;
+        const char* nhbuf = ring + nh * kUnitBytes;
         lm_mma_with(now, acc, [&](int m) {
 #pragma unroll
-          for (int u = 0; u < kFillsPerMfma; ++u)
-            if (m * kFillsPerMfma + u < kLoads) lm_fill1(fill, fbase, fstage, m * kFillsPerMfma + u);
-          if (m < kXB + kYB) lm_read1(next, nbuf, off_w[0], off_h[0], m);
+          for (int q = 0; q < kFillsPerMfma; ++q) {
+            const int r = m * kFillsPerMfma + q;
+            if (r < kLoadsU) {
+              if (!TAIL || sa < ns) lm_fill1(fill, fa, sa, kSlots % 2 == 0, r);
+            } else if (r < kLoads) {
+              if (!TAIL || sb < ns) lm_fill1(fill, fb, sb, kSlots % 2 == 1, r - kLoadsU);
+            }
+          }
+          if (m < kXB + kYB) lm_read1(next, nwbuf, nhbuf, off_w[0], off_h[0], m);
         });
       }
     }
-    cur = nxt;
-  }
+    sw = nw;
+  };
+  int s = 0;
+  for (; s < ns - kTail; ++s) stage(s, std::false_type());
+  for (; s < ns; ++s) stage(s, std::true_type());
   wait_counts<0, 15>();   // no request may still be writing LDS when the workgroup ends
+  lds_barrier();          // every wave is done with the ring: the epilogues reuse it
 
   const int64_t wrow0 = v0 + kWV * wv;     // first vocabulary row of this wave
   if constexpr (GRAD) {
@@ -465,9 +506,8 @@ void lmhead_kernel(LmArgs p) {
     // labels.  The tile goes through LDS (the ring is free now) as bf16
     // [vocab row][token], 16-byte chunks of a row XOR-swizzled by the row, so
     // that it leaves as whole 16-byte vectors of 8 tokens: vocabulary-major.
-    static_assert(kTV * kTN * 2 <= kRing * kStageBytes, "grad tile fits the ring");
+    static_assert(kTV * kTN * 2 <= kRingBytes, "grad tile fits the ring");
     constexpr int kTileRowBytes = kTN * 2;
-    lds_barrier();   // every wave is done reading the ring
 #pragma unroll
     for (int y = 0; y < kYB; ++y) {
       const int tok = kWN * wt + 32 * y + lr;   // token within the tile
@@ -478,21 +518,17 @@ void lmhead_kernel(LmArgs p) {
       const bool bad = !ignored && (lb < 0 || lb >= p.vocab);
       const float lse = p.lse[j];
       const float w = p.token_weights ? p.token_weights[j] : 1.0f;
-      const int64_t yl = lb - p.vocab_offset;   // the label's row among these lm_head rows
+      // the label's row within this tile, or -1
+      const int64_t yl = lb - p.vocab_offset - v0;
+      const int ylr = yl >= 0 && yl < kTV ? int(yl) : -1;
 #pragma unroll
       for (int x = 0; x < kXB; ++x)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = kWV * wv + 32 * x + 8 * (r >> 2) + 4 * half + (r & 3);
-          float g;
-          if (ignored) {
-            g = 0.0f;
-          } else if (bad) {
-            g = NAN;
-          } else {
-            const float pr = exp2_hw((acc[x][y][r] - lse) * kLog2e);
-            g = v0 + row == yl ? w * (pr - 1.0f) : w * pr;
-          }
+          const float pr = exp2_hw((acc[x][y][r] - lse) * kLog2e);
+          float g = row == ylr ? w * (pr - 1.0f) : w * pr;
+          g = ignored ? 0.0f : (bad ? NAN : g);
           const int at = row * kTileRowBytes + ((((tok >> 3) ^ (row & 31)) << 4) | ((tok & 7) << 1));
           *reinterpret_cast<__bf16*>(ring + at) = __bf16(g);
         }
@@ -523,7 +559,9 @@ void lmhead_kernel(LmArgs p) {
     return;
   }
 
-  lm_stats_epilogue(p, acc, lab, tv, tn, wv, wt, lr, half, red);
+  typedef float Red[kWT][kYB][32][4];
+  static_assert(sizeof(Red) <= kRingBytes, "reduction fits the ring");
+  lm_stats_epilogue(p, acc, lab, tv, tn, wv, wt, lr, half, *reinterpret_cast<Red*>(ring));
 }
 
 // Shared validation of the lm_head entry points; fills the common arguments.
