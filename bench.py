@@ -36,7 +36,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-rows", type=int, default=4096)
+    ap.add_argument("--cpu-sample-rows", type=int, default=32768)
     ap.add_argument("--profile-steps", type=int, default=None,
                     help="run only this many steps (for profilers); still prints the line")
     ap.add_argument("--no-lmhead", action="store_true",
@@ -184,7 +184,7 @@ def lmhead_leg(bi, torch, np, wl, N, V, seed, steps, warm, stream, with_cpu=True
             "cpu_baseline": cpu}
 
 
-def lmhead_cpu_baseline(b, np, wl, sample=256):
+def lmhead_cpu_baseline(b, np, wl, sample=2048):
     """The fp64 oracle on the first `sample` tokens of the lm_head workload: forward
     (logits, logprob, entropy) and backward (the gradient of the logits, grad_hidden
     and those tokens' grad_weight terms), full vocabulary and hidden size."""
