@@ -508,12 +508,23 @@ __device__ inline void bwd_vec(const RowDst<GT, Elt<DT>::VEC>& dst, uint32_t k, 
   dst.template store<VSTORE>(k, g);
 }
 
-template <int DT, int GT, bool VLOAD, bool VSTORE, int POL = kNonTemporal, bool REV = false>
+// Vectors per lane per load group in the backward (the next group's loads
+// are in flight while one is written).  The backward is elementwise, so this
+// is pure pipelining and changes no result bit: for bf16 logits and bf16
+// gradients in the kernels built for aligned rows (DEEP), 3 (24 elements) was
+// the fastest depth that keeps the fused kernel within its 64 registers; the
+// other kernels keep the rescale group's size.
+template <int DT, int GT, bool DEEP>
+constexpr int kBwdGroup =
+    (DEEP && DT == BI_BF16 && GT == BI_BF16) ? 3 : kGroupElems / Elt<DT>::VEC;
+
+template <int DT, int GT, bool VLOAD, bool VSTORE, int POL = kNonTemporal, bool REV = false,
+          bool DEEP = false>
 __device__ inline void bwd_row(const BwdArgs& p, const RowSrc& src,
                                const RowDst<GT, Elt<DT>::VEC>& dst, int64_t y, int kind,
                                float lse, float w, int T, int tid) {
   constexpr int VEC = Elt<DT>::VEC;
-  constexpr int G = kGroupElems / VEC;
+  constexpr int G = kBwdGroup<DT, GT, DEEP>;
   const int64_t width = p.vocab;
   const uint32_t nfull = uint32_t(width / VEC);
   const uint32_t nvec = uint32_t((width + VEC - 1) / VEC);
@@ -588,7 +599,8 @@ void bwd_kernel(BwdArgs p) {
     const bool vload = ALIGNED || (reinterpret_cast<uintptr_t>(rp) & 3u) == 0;
     const bool vstore = ALIGNED || (reinterpret_cast<uintptr_t>(gp) & 3u) == 0;
     if (ALIGNED || (vload && vstore)) {
-      bwd_row<DT, GT, true, true>(p, src, dst, y, kind, lse, w, T, tid);
+      bwd_row<DT, GT, true, true, kNonTemporal, false, ALIGNED>(p, src, dst, y, kind, lse, w,
+                                                                 T, tid);
     } else if (vload) {
       bwd_row<DT, GT, true, false>(p, src, dst, y, kind, lse, w, T, tid);
     } else if (vstore) {
@@ -721,7 +733,7 @@ void fused_reread_kernel(FusedArgs p) {
     BwdArgs b{p.logits, p.grad, p.n_rows, width, p.row_bytes, p.grad_row_bytes, p.labels,
               p.ignore_index, nullptr, nullptr, nullptr};
     if (ALIGNED || (vload && vstore))
-      bwd_row<DT, GT, true, true, P2, REV>(b, src, dst, y, kind, lse, w, T, tid);
+      bwd_row<DT, GT, true, true, P2, REV, ALIGNED>(b, src, dst, y, kind, lse, w, T, tid);
     else if (vload)
       bwd_row<DT, GT, true, false, P2, REV>(b, src, dst, y, kind, lse, w, T, tid);
     else if (vstore)
