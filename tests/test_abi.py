@@ -7,6 +7,8 @@ HIP work is ever queued.
 import ctypes
 import os
 import re
+import shutil
+import subprocess
 
 import pytest
 
@@ -263,3 +265,25 @@ def test_python_binding_rejects_host_tensors():
         bi.fwd(x, y)
     with pytest.raises(ValueError):
         bi.vocab_chunk_stats(x, y, 0, None)
+
+
+def test_a_c_program_links_and_calls_the_abi(tmp_path):
+    # the header as C99 (-pedantic, warnings are errors) and the library linked
+    # into a C executable; the program calls host-side entry points only
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no gcc")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    libdir = os.path.dirname(bi.library_path())
+    exe = str(tmp_path / "abi_consumer")
+    cmd = [gcc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror",
+           "-I", os.path.join(root, "include"), os.path.join(root, "tests", "c", "abi_consumer.c"),
+           "-L", libdir, "-lbi_logprob", "-Wl,-rpath," + libdir,
+           "-Wl,-rpath-link,/opt/rocm/lib", "-o", exe]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    env = dict(os.environ)
+    env["LD_LIBRARY_PATH"] = "/opt/rocm/lib:" + env.get("LD_LIBRARY_PATH", "")
+    r = subprocess.run([exe], capture_output=True, text=True, env=env, timeout=60)
+    assert r.returncode == 0, (r.returncode, r.stdout, r.stderr)
+    assert "1024 threads" in r.stdout and "bi_logprob_fwd(n_rows = -1)" in r.stdout
