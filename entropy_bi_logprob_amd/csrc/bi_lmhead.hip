@@ -1,7 +1,9 @@
 // bi_lmhead.hip - the lm_head projection on the CDNA4 matrix cores, fused with
 // the per-token statistics of each vocabulary tile, so the [N, V] logits never
-// reach HBM.  C ABI: bi_lmhead_tile_stats, bi_lmhead_tiles, bi_lmhead_tile_rows
-// (include/bi_logprob.h); bi_stats_combine finishes.
+// reach HBM, and with the gradient of those logits for the backward.  C ABI:
+// bi_lmhead_tile_stats, bi_lmhead_grad_logits, bi_lmhead_tiles,
+// bi_lmhead_tile_rows (include/bi_logprob.h); bi_stats_combine finishes the
+// statistics and bi_lmhead_backward (bi_lmhead_bwd.hip) the backward.
 //
 // What is computed: the chunked lm_head of "ZeroSyncGRPOTrainer" (logits of a
 // vocabulary slice from the hidden states and the replicated projection, bf16
@@ -19,15 +21,18 @@
 //    128 x 64 part (4 x 2 blocks, 128 accumulators).  The 256 x 256 tile keeps
 //    the operand bytes streamed from L2 per MFMA at their minimum for what the
 //    register file can hold.
-//  * K runs in stages of 64 through a 2-deep LDS ring (64 KB per stage) filled
+//  * K runs in stages of 64, each stage two 32 KB units (its 256 W rows, its
+//    256 H rows) streamed through a FIFO of LDS slots: four slots are a 2-deep
+//    ring of whole stages (a fifth is a build option).  Units are filled
 //    straight from global memory (global_load_lds_dwordx4, no register
 //    staging).  A stage is 4 MFMA K steps; each step's MFMAs are issued one by
 //    one with the next step's fragment reads between them.  Before the last
 //    step each wave waits for its own requests of stage s+1 and for its LDS
 //    reads of stage s, and the one barrier per stage both publishes stage s+1
-//    and frees stage s's buffer; the requests for stage s+2 are then spread
+//    and frees stage s's slots; the requests that refill them are then spread
 //    between the last step's MFMAs, so the matrix pipe keeps running while
-//    they issue.
+//    they issue.  The loop body has no branch; the last stages, whose refills
+//    would lie past the end, run in a separate tail loop.
 //  * LDS rows are 128 bytes (8 chunks of 8 bf16).  Chunk c of row r is stored
 //    in slot c ^ g(r), g(r) = (r ^ ((r >> 3) & 3)) & 7, which puts the 8- and
 //    16-lane groups of every ds_read_b128 on distinct banks.  The shape knobs
