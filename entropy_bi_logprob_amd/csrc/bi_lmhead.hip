@@ -404,12 +404,19 @@ void lmhead_kernel(LmArgs p) {
   const int64_t v0 = tv * kTV, n0 = tn * kTN;
   const int lr = lane & 31, half = lane >> 5;
 
-  // the labels of this lane's tokens, fetched early (used by the epilogue)
+  // the labels of this lane's tokens (and for the gradient their lse and
+  // weight), fetched early: the epilogue uses them once the K loop is done
   int64_t lab[kYB];
+  float tlse[kYB], tw[kYB];
 #pragma unroll
   for (int y = 0; y < kYB; ++y) {
     const int64_t j = n0 + kWN * wt + 32 * y + lr;
-    lab[y] = j < p.n_tok ? p.labels[j] : p.ignore_index;
+    const bool in = j < p.n_tok;
+    lab[y] = in ? p.labels[j] : p.ignore_index;
+    if constexpr (GRAD) {
+      tlse[y] = in ? p.lse[j] : 0.0f;
+      tw[y] = in && p.token_weights ? p.token_weights[j] : 1.0f;
+    }
   }
 
   const LmFill fill = lm_fill_setup(p, v0, n0, wave, lane);
@@ -521,8 +528,8 @@ void lmhead_kernel(LmArgs p) {
       const int64_t lb = lab[y];
       const bool ignored = lb == p.ignore_index;
       const bool bad = !ignored && (lb < 0 || lb >= p.vocab);
-      const float lse = p.lse[j];
-      const float w = p.token_weights ? p.token_weights[j] : 1.0f;
+      const float lse = tlse[y];
+      const float w = tw[y];
       // the label's row within this tile, or -1
       const int64_t yl = lb - p.vocab_offset - v0;
       const int ylr = yl >= 0 && yl < kTV ? int(yl) : -1;
