@@ -196,6 +196,42 @@ def test_backward_against_oracle(n, vc, d, chunk, gdt):
     _check_grads(host(gh), host(gw.float()), G, h, w, gdt == torch.bfloat16)
 
 
+def _padded(t, extra):
+    # the same values in rows `extra` elements longer (a column slice of a wider buffer)
+    wide = torch.zeros((t.shape[0], t.shape[1] + extra), dtype=t.dtype, device=t.device)
+    wide[:, :t.shape[1]] = t
+    return wide[:, :t.shape[1]]
+
+
+def test_padded_row_strides_give_the_same_bits():
+    n, vc, d = 300, 1000, 192
+    b, H, W, labels, h, w, olse, tw = _setup(n, vc, d, seed=17)
+    Hp, Wp = _padded(H, 64), _padded(W, 136)
+    assert Hp.stride(0) == d + 64 and Wp.stride(0) == d + 136
+    st = bi.lmhead_tile_stats(H, W, labels)
+    stp = bi.lmhead_tile_stats(Hp, Wp, labels)
+    _, _, lse = bi.stats_combine(st, labels)
+    twd = dev(tw)
+    g = bi.lmhead_grad_logits(H, W, labels, lse, twd)
+    gp = bi.lmhead_grad_logits(Hp, Wp, labels, lse, twd)
+    # gradient rows padded too: a stride that is a multiple of 8 (16-byte
+    # vector stores) and an odd one (the element path, as for n = 300 itself)
+    g8 = _padded(torch.empty_like(g), 44)
+    g3 = _padded(torch.empty_like(g), 3)
+    assert g8.stride(0) % 8 == 0 and g3.stride(0) % 2 == 1
+    bi.lmhead_grad_logits(H, W, labels, lse, twd, out=g8)
+    bi.lmhead_grad_logits(H, W, labels, lse, twd, out=g3)
+    torch.cuda.synchronize()
+    assert torch.equal(st.view(torch.int32), stp.view(torch.int32))
+    for other in (gp, g8, g3):
+        assert torch.equal(g.contiguous().view(torch.int16), other.contiguous().view(torch.int16))
+    # the backward with padded operands: the library GEMMs take the strides
+    gh, gw = bi.lmhead_backward(Hp, Wp, labels, lse, twd, chunk_rows=512)
+    torch.cuda.synchronize()
+    G = orc.lmhead_backward(h, w, b.labels, host(lse), tw)
+    _check_grads(host(gh), host(gw.float()), G, h, w, True)
+
+
 def test_backward_accumulates_over_vocabulary_shards():
     n, vc, d = 200, 1000, 128
     b, H, W, labels, h, w, olse, tw = _setup(n, vc, d, seed=17)
