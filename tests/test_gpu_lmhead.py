@@ -78,6 +78,36 @@ def test_many_tiles_per_workgroup(n, vc, d):
     assert_close(host(lse), olse, TOL, "lse")
 
 
+def test_largest_hidden_size():
+    # d = 2^22, the largest the lm_head entry points accept: a load's 32-bit
+    # offset from its tile's base reaches 255 rows x 2^23 bytes, and the K loop
+    # runs 65,536 stages; 300 lm_head rows make one full and one ragged tile.
+    # Sparse +-1 rows keep every logit an exact small integer, so the usual
+    # tolerances apply; the oracle sees only the columns that are nonzero
+    # somewhere (the others add exact zeros).
+    n, vc, d = 8, 300, 1 << 22
+    b = wl.sparse_lmhead_batch(n, vc, d, seed=23)
+    H, W, labels = to_dev_bf16(b.hidden), to_dev_bf16(b.weight), dev(b.labels)
+    cols = np.nonzero((b.hidden != 0).any(axis=0) | (b.weight != 0).any(axis=0))[0]
+    assert cols[-1] == d - 1
+    h, w = orc.decode(b.hidden[:, cols], "bf16"), orc.decode(b.weight[:, cols], "bf16")
+    z = orc.lmhead_logits(h, w)
+    olp, oent, olse = orc.forward(z, b.labels)
+    lse_in, lse_o = _saved_lse(olse)
+    tw = np.full(n, 0.5, dtype=np.float32)
+    st = bi.lmhead_tile_stats(H, W, labels)
+    lp, ent, lse = bi.stats_combine(st, labels)
+    g = bi.lmhead_grad_logits(H, W, labels, lse_in, dev(tw))
+    torch.cuda.synchronize()
+    check_tiles(host(st), orc.lmhead_tile_stats(h, w, b.labels, 0, vc, bi.lmhead_tile_rows()))
+    assert_close(host(lp), olp, TOL, "logprob")
+    assert_close(host(ent), oent, TOL, "entropy")
+    assert_close(host(lse), olse, TOL, "lse")
+    G = orc.backward(z, b.labels, lse_o, tw)
+    got = orc.decode(host(g.view(torch.int16)).view(np.uint16), "bf16").T
+    assert np.all(np.abs(got - G) <= 1e-5 * 0.5 + ulp_bf16(G))
+
+
 def test_tiles_do_not_depend_on_the_batch():
     n, vc, d = 640, 1500, 256
     b = wl.lmhead_batch(n, vc, d, seed=3)
@@ -138,18 +168,24 @@ def _setup(n, vc, d, seed, ignore_frac=0.1):
     return b, H, W, labels, h, w, olse, tw
 
 
+def _saved_lse(olse):
+    # the lse a forward pass saves, in fp32: the oracle's, so that the GPU
+    # backward and the oracle's take the same input
+    lse32 = olse.astype(np.float32)
+    return dev(lse32), lse32.astype(np.float64)
+
+
 @pytest.mark.parametrize("n,vc,d", [(300, 1000, 128), (77, 333, 256), (513, 257, 192),
                                     (5, 130, 64)])
 def test_grad_logits_against_oracle(n, vc, d):
     b, H, W, labels, h, w, olse, tw = _setup(n, vc, d, seed=n + vc)
-    # the lse as the forward path produces it
-    _, _, lse = bi.lmhead_logprob(H, W, labels)
+    lse, lse_o = _saved_lse(olse)
     g = bi.lmhead_grad_logits(H, W, labels, lse, dev(tw))
     torch.cuda.synchronize()
-    G, _, _ = orc.lmhead_backward(h, w, b.labels, host(lse), tw)
+    G, _, _ = orc.lmhead_backward(h, w, b.labels, lse_o, tw)
     got = orc.decode(host(g.view(torch.int16)).view(np.uint16), "bf16").T   # [n, vc]
-    # fp32 logits and lse: |dp| <~ 1e-5 p; then one bf16 rounding (at most one
-    # ulp of the exact value, whichever binade the computed value falls in)
+    # fp32 logits: |dp| <~ 1e-5 p; then one bf16 rounding (at most one ulp of
+    # the exact value, whichever binade the computed value falls in)
     bound = 1e-5 * np.abs(tw)[:, None] + ulp_bf16(G)
     assert np.all(np.abs(got - G) <= bound), float(np.max(np.abs(got - G) - bound))
     ign = b.labels == -100
@@ -188,11 +224,11 @@ def _check_grads(gh, gw, G, h, w, gw_bf16):
 @pytest.mark.parametrize("gdt", [torch.float32, torch.bfloat16], ids=["gw_f32", "gw_bf16"])
 def test_backward_against_oracle(n, vc, d, chunk, gdt):
     b, H, W, labels, h, w, olse, tw = _setup(n, vc, d, seed=n + d)
-    _, _, lse = bi.lmhead_logprob(H, W, labels)
+    lse, lse_o = _saved_lse(olse)
     gh, gw = bi.lmhead_backward(H, W, labels, lse, dev(tw), grad_weight_dtype=gdt,
                                 chunk_rows=chunk)
     torch.cuda.synchronize()
-    G = orc.lmhead_backward(h, w, b.labels, host(lse), tw)
+    G = orc.lmhead_backward(h, w, b.labels, lse_o, tw)
     _check_grads(host(gh), host(gw.float()), G, h, w, gdt == torch.bfloat16)
 
 
@@ -210,7 +246,7 @@ def test_padded_row_strides_give_the_same_bits():
     assert Hp.stride(0) == d + 64 and Wp.stride(0) == d + 136
     st = bi.lmhead_tile_stats(H, W, labels)
     stp = bi.lmhead_tile_stats(Hp, Wp, labels)
-    _, _, lse = bi.stats_combine(st, labels)
+    lse, lse_o = _saved_lse(olse)
     twd = dev(tw)
     g = bi.lmhead_grad_logits(H, W, labels, lse, twd)
     gp = bi.lmhead_grad_logits(Hp, Wp, labels, lse, twd)
@@ -228,14 +264,14 @@ def test_padded_row_strides_give_the_same_bits():
     # the backward with padded operands: the library GEMMs take the strides
     gh, gw = bi.lmhead_backward(Hp, Wp, labels, lse, twd, chunk_rows=512)
     torch.cuda.synchronize()
-    G = orc.lmhead_backward(h, w, b.labels, host(lse), tw)
+    G = orc.lmhead_backward(h, w, b.labels, lse_o, tw)
     _check_grads(host(gh), host(gw.float()), G, h, w, True)
 
 
 def test_backward_accumulates_over_vocabulary_shards():
     n, vc, d = 200, 1000, 128
     b, H, W, labels, h, w, olse, tw = _setup(n, vc, d, seed=17)
-    _, _, lse = bi.lmhead_logprob(H, W, labels)
+    lse, lse_o = _saved_lse(olse)
     twd = dev(tw)
     gh_full, gw_full = bi.lmhead_backward(H, W, labels, lse, twd, grad_weight_dtype=torch.float32)
     # two shards (one split inside a 256-row tile) adding into one grad_hidden
@@ -245,7 +281,7 @@ def test_backward_accumulates_over_vocabulary_shards():
     _, gwb = bi.lmhead_backward(H, W[300:].contiguous(), labels, lse, twd, 300, vc,
                                 grad_hidden=gh, grad_weight_dtype=torch.float32)
     torch.cuda.synchronize()
-    G = orc.lmhead_backward(h, w, b.labels, host(lse), tw)
+    G = orc.lmhead_backward(h, w, b.labels, lse_o, tw)
     _check_grads(host(gh), host(torch.cat([gwa, gwb])), G, h, w, False)
     _check_grads(host(gh_full), host(gw_full), G, h, w, False)
 

@@ -36,7 +36,8 @@ def sample_rows(n, k, seed=7):
     return np.array(sorted(rows))
 
 
-def check_grads(b, rows, lse_gpu, g32_rows, gb16_rows=None):
+def check_grads(b, rows, g32_rows, gb16_rows=None):
+    # the oracle's gradient from its own lse, against the GPU's end to end
     tg = TOL[b.dtype][2]
     z = orc.decode(b.logits[rows], b.dtype)
     _, _, olse = orc.forward(z, b.labels[rows])
@@ -77,7 +78,7 @@ def test_fwdbwd_4096_bf16():
     assert_close(host(ent), oent, te, "entropy")
     rows = sample_rows(4096, 48)
     ridx = torch.from_numpy(rows).cuda()
-    check_grads(b, rows, host(lse)[rows], host(g32[ridx]), host(g16[ridx]))
+    check_grads(b, rows, host(g32[ridx]), host(g16[ridx]))
 
 
 def test_masked_2048_f32_odd_width():
@@ -94,7 +95,7 @@ def test_masked_2048_f32_odd_width():
     masked = torch.isneginf(logits)
     assert int((g[masked] != 0).sum()) == 0
     rows = sample_rows(2048, 32)
-    check_grads(b, rows, host(lse)[rows], host(g[torch.from_numpy(rows).cuda()]))
+    check_grads(b, rows, host(g[torch.from_numpy(rows).cuda()]))
 
 
 # ------------------------------------------------------------ batch invariance
@@ -134,7 +135,7 @@ def test_batch_invariance_sweep(fused):
     tl, te, _ = TOL["bf16"]
     assert_close(host(ref[0]), olp, tl, "logprob")
     assert_close(host(ref[1]), oent, te, "entropy")
-    check_grads(core, np.arange(16), None, host(ref[4]), host(ref[3]))
+    check_grads(core, np.arange(16), host(ref[4]), host(ref[3]))
 
 
 def test_chunk_and_multi_paths_are_batch_invariant():
@@ -223,7 +224,7 @@ def test_large_fwd_bwd_sampled_rows(large):
     assert_close(host(lp)[rows], olp, tl, "logprob")
     assert_close(host(ent)[rows], oent, te, "entropy")
     assert_close(host(lse)[rows], olse, tl, "lse")
-    check_grads(b, rows, None, host(g32), host(g16[ridx]))
+    check_grads(b, rows, host(g32), host(g16[ridx]))
     assert np.all(np.isfinite(host(lp))) and np.all(np.isfinite(host(ent)))
 
 

@@ -298,3 +298,27 @@ def lmhead_batch(n: int, vocab: int, d: int, seed: int = DEFAULT_SEED, sigma: fl
     if k:
         labels[g.choice(n, size=k, replace=False)] = IGNORE_INDEX
     return LmheadBatch(hidden, weight, labels)
+
+
+def sparse_lmhead_batch(n: int, vocab: int, d: int, seed: int = DEFAULT_SEED, nnz: int = 64,
+                        pool: int = 1024) -> LmheadBatch:
+    """Hidden and lm_head rows (bf16 bits) that are zero except for ``nnz``
+    entries of +1 or -1 per row, at columns drawn from one seeded pool of
+    ``pool`` columns spread over [0, d) that always holds column d - 1.  Every
+    logit is then a small integer, which fp32 accumulates exactly at any d:
+    inputs for the largest hidden sizes, where dense random rows would make the
+    logits' own rounding the subject of the test."""
+    g = np.random.default_rng([seed, 800, n, vocab, d])
+    cols = np.unique(np.concatenate([g.choice(d, size=pool - 1, replace=False), [d - 1]]))
+    one, minus_one = f32_to_bf16_bits(np.array([1.0, -1.0], dtype=np.float32))
+
+    def fill(rows):
+        out = np.zeros((rows, d), dtype=np.uint16)
+        for r in range(rows):
+            c = g.choice(cols, size=min(nnz, cols.size), replace=False)
+            out[r, c] = np.where(g.random(c.size) < 0.5, one, minus_one)
+        return out
+
+    hidden, weight = fill(n), fill(vocab)
+    labels = g.integers(0, vocab, size=n).astype(np.int64)
+    return LmheadBatch(hidden, weight, labels)
