@@ -210,13 +210,16 @@ __device__ inline uint32_t lds_addr(const char* p) {
 }
 
 // Request i of one unit: operand W (is_w) or H, K stage `stage`, into the
-// slot at LDS address `slot`.  Written as inline
-// assembly so that the compiler does not track these LDS writes: it would
-// otherwise wait for every request in flight before any LDS read.  The waits
-// are explicit instead (wait_counts before each barrier); the compiler's own
-// vmcnt waits stay correct, since extra requests only make them stricter.
-// The LDS-DMA load reads M0, which the compiler writes just before the asm
-// with a scalar instruction: one wait state (s_nop 0) must separate the two.
+// slot at LDS address `slot`.  The byte offset from the tile's base fits 31
+// bits: row <= 255, the row pitch is at most 2^23 bytes and stage * kRowBytes
+// below 2^23 (the entry points cap d and the strides at 2^22 elements).
+// Written as inline assembly so that the compiler does not track these LDS
+// writes: it would otherwise wait for every request in flight before any LDS
+// read.  The waits are explicit instead (wait_counts before each barrier);
+// the compiler's own vmcnt waits stay correct, since extra requests only make
+// them stricter.  The LDS-DMA load reads M0, which the compiler writes just
+// before the asm with a scalar instruction: one wait state (s_nop 0) must
+// separate the two.
 __device__ inline void lm_fill1(const LmFill& f, uint32_t slot, int stage, bool is_w, int i) {
   const int row = min(f.row0 + kBlockRows * kWaves * i, is_w ? f.wlast : f.hlast);
   const uint32_t off = uint32_t(row) * (is_w ? f.ldw2 : f.ldh2) + f.cbytes +
