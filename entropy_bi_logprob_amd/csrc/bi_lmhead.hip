@@ -22,17 +22,19 @@
 //    the operand bytes streamed from L2 per MFMA at their minimum for what the
 //    register file can hold.
 //  * K runs in stages of 64, each stage two 32 KB units (its 256 W rows, its
-//    256 H rows) streamed through a FIFO of LDS slots: four slots are a 2-deep
-//    ring of whole stages (a fifth is a build option).  Units are filled
-//    straight from global memory (global_load_lds_dwordx4, no register
-//    staging).  A stage is 4 MFMA K steps; each step's MFMAs are issued one by
-//    one with the next step's fragment reads between them.  Before the last
-//    step each wave waits for its own requests of stage s+1 and for its LDS
-//    reads of stage s, and the one barrier per stage both publishes stage s+1
-//    and frees stage s's slots; the requests that refill them are then spread
-//    between the last step's MFMAs, so the matrix pipe keeps running while
-//    they issue.  The loop body has no branch; the last stages, whose refills
-//    would lie past the end, run in a separate tail loop.
+//    256 H rows) streamed through a FIFO of five LDS slots (all 160 KB).
+//    Units are filled straight from global memory (global_load_lds_dwordx4,
+//    no register staging).  A stage is 4 MFMA K steps; each step's MFMAs are
+//    issued one by one with the next step's fragment reads between them.
+//    Before the last step each wave waits for its own requests of stage s+1
+//    and for its LDS reads of stage s, and the one barrier per stage both
+//    publishes stage s+1 and frees stage s's slots.  Stage s+2's H unit is
+//    then requested between the last step's MFMAs, and its W unit, which
+//    has a stage longer to land, between the next stage's first steps: the
+//    requests never arrive in one burst that would hold up the MFMAs queued
+//    behind them.  The loop body has no branch; the last stages, whose
+//    refills would lie past the end, run in a separate tail loop.  (Four
+//    slots, a 2-deep ring of whole stages, remain a build option.)
 //  * LDS rows are 128 bytes (8 chunks of 8 bf16).  Chunk c of row r is stored
 //    in slot c ^ g(r), g(r) = (r ^ ((r >> 3) & 3)) & 7, which puts the 8- and
 //    16-lane groups of every ds_read_b128 on distinct banks.  The shape knobs
@@ -62,7 +64,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // Tuning knobs (shape of the pipeline only; every choice computes the same
 // statistics tile of 256 vocabulary rows, bit for bit).
 #ifndef BI_LM_SLOTS
-#define BI_LM_SLOTS 4      // LDS slots of one operand's stage: 4 (two whole stages) or 5
+#define BI_LM_SLOTS 5      // LDS slots of one operand's stage: 5, or 4 (two whole stages)
 #endif
 #ifndef BI_LM_GROUP
 #define BI_LM_GROUP 8      // token tiles that sweep the vocabulary together
@@ -442,14 +444,22 @@ void lmhead_kernel(LmArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[x][y][r] = 0.0f;
 
-  // prologue: units 0 .. kSlots-1 requested, stage 0 (units 0 and 1) landed
-  // and visible
+  // With five slots the W unit of stage s+2 (unit 2s+4) is requested during
+  // stage s's first kKS-1 steps, a few requests per step, instead of right
+  // after a barrier: only stage s+2's H unit goes out then.  (All waves
+  // requesting a whole stage at once after each barrier holds up the MFMAs
+  // that are ordered after those requests.)
+  constexpr bool kSpread = kSlots == 5;
+  constexpr int kPrologue = kSpread ? kSlots - 1 : kSlots;
+
+  // prologue: units 0 .. kPrologue-1 requested, stage 0 (units 0 and 1)
+  // landed and visible
   const uint32_t rbase = lds_addr(ring);
 #pragma unroll
-  for (int u = 0; u < kSlots; ++u)
+  for (int u = 0; u < kPrologue; ++u)
 #pragma unroll
     for (int i = 0; i < kLoadsU; ++i) lm_fill_unit1(fill, rbase, u, ns, i);
-  wait_units(min(kSlots, 2 * ns) - 2);   // units 2 .. min(kSlots, 2 ns) - 1 may fly on
+  wait_units(min(kPrologue, 2 * ns) - 2);   // units 2 .. min(kPrologue, 2 ns) - 1 may fly on
   lds_barrier();
   LmFrag fr[2];
   lm_read(fr[0], ring, ring + kUnitBytes, off_w[0], off_h[0]);
@@ -473,6 +483,10 @@ void lmhead_kernel(LmArgs p) {
     const int nh = nw + 1 == kSlots ? 0 : nw + 1;
     const char* wbuf = ring + sw * kUnitBytes;
     const char* hbuf = ring + sh * kUnitBytes;
+    // spread: unit 2s+4 (W of stage s+2) into the slot before sw, freed at
+    // the previous barrier
+    const uint32_t fp = rbase + uint32_t(sw == 0 ? kSlots - 1 : sw - 1) * kUnitBytes;
+    const bool pending = !TAIL || s + 2 < ns;
 #pragma unroll
     for (int kk = 0; kk < kKS; ++kk) {
       LmFrag& now = fr[kk & 1];
@@ -480,6 +494,14 @@ void lmhead_kernel(LmArgs p) {
       if (kk + 1 < kKS) {
         lm_mma_with(now, acc, [&](int m) {
           if (m < kXB + kYB) lm_read1(next, wbuf, hbuf, off_w[kk + 1], off_h[kk + 1], m);
+          if constexpr (kSpread) {
+            // request r goes out in step r (kKS-1) / kLoadsU, after the step's reads
+#pragma unroll
+            for (int r = 0; r < kLoadsU; ++r)
+              if (r * (kKS - 1) / kLoadsU == kk &&
+                  m == kXB + kYB + r - (kk * kLoadsU + kKS - 2) / (kKS - 1) && pending)
+                lm_fill1(fill, fp, s + 2, true, r);
+          }
         });
       } else {
         // units requested so far: 0 .. min(2s + kSlots, 2ns) - 1
@@ -493,13 +515,20 @@ void lmhead_kernel(LmArgs p) {
         const char* nwbuf = ring + nw * kUnitBytes;
         const char* nhbuf = ring + nh * kUnitBytes;
         lm_mma_with(now, acc, [&](int m) {
+          if constexpr (kSpread) {
+            // only unit 2s+5 (H of stage s+2) now, every other MFMA; unit
+            // 2s+6 is the next stage's spread W unit
+            if (m % 2 == 0 && m / 2 < kLoadsU && (!TAIL || sa < ns))
+              lm_fill1(fill, fa, sa, false, m / 2);
+          } else {
 #pragma unroll
-          for (int q = 0; q < kFillsPerMfma; ++q) {
-            const int r = m * kFillsPerMfma + q;
-            if (r < kLoadsU) {
-              if (!TAIL || sa < ns) lm_fill1(fill, fa, sa, kSlots % 2 == 0, r);
-            } else if (r < kLoads) {
-              if (!TAIL || sb < ns) lm_fill1(fill, fb, sb, kSlots % 2 == 1, r - kLoadsU);
+            for (int q = 0; q < kFillsPerMfma; ++q) {
+              const int r = m * kFillsPerMfma + q;
+              if (r < kLoadsU) {
+                if (!TAIL || sa < ns) lm_fill1(fill, fa, sa, kSlots % 2 == 0, r);
+              } else if (r < kLoads) {
+                if (!TAIL || sb < ns) lm_fill1(fill, fb, sb, kSlots % 2 == 1, r - kLoadsU);
+              }
             }
           }
           if (m < kXB + kYB) lm_read1(next, nwbuf, nhbuf, off_w[0], off_h[0], m);
