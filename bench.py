@@ -128,7 +128,7 @@ def lmhead_leg(bi, torch, np, wl, N, V, seed, steps, warm, stream, with_cpu=True
     gh = torch.zeros((N, d), dtype=torch.float32, device=dev)
     gw = torch.empty((V, d), dtype=torch.bfloat16, device=dev)
     chunk = 32768
-    ws = torch.empty(int(bi.lib().bi_lmhead_backward_workspace(N, chunk)), dtype=torch.uint8,
+    ws = torch.empty(int(bi.lib().bi_lmhead_backward_workspace(N, d, chunk)), dtype=torch.uint8,
                      device=dev)
     (t_bwd,) = timed([lambda: bi.lmhead_backward(H, W, labels, lse, tw, grad_hidden=gh,
                                                  grad_weight=gw, workspace=ws, stream=stream)])

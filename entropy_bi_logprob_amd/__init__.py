@@ -102,7 +102,7 @@ def lib() -> ctypes.CDLL:
     L.bi_lmhead_backward.argtypes = [vp, vp, i64, i64, i64, i64, i64, i64, i64, vp, i64, vp, vp,
                                      vp, i64, vp, i32, i64, vp, i64, vp, vp]
     L.bi_lmhead_backward.restype = i32
-    L.bi_lmhead_backward_workspace.argtypes = [i64, i64]
+    L.bi_lmhead_backward_workspace.argtypes = [i64, i64, i64]
     L.bi_lmhead_backward_workspace.restype = i64
     L.bi_stats_combine.argtypes = [vp, i64, i64, vp, i64, vp, vp, vp, vp]
     L.bi_row_geometry.argtypes = [i32, i64, ctypes.POINTER(i32), ctypes.POINTER(i32),
@@ -448,7 +448,7 @@ def lmhead_backward(hidden: torch.Tensor, weight: torch.Tensor, labels: torch.Te
         raise ValueError(f"grad_weight must be a [{vc}, {d}] tensor")
     L = lib()
     if workspace is None:
-        nbytes = int(L.bi_lmhead_backward_workspace(n, min(chunk_rows, max(vc, 1))))
+        nbytes = int(L.bi_lmhead_backward_workspace(n, d, min(chunk_rows, max(vc, 1))))
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     _check("bi_lmhead_backward", L.bi_lmhead_backward(
         _ptr(hidden), _ptr(weight), n, vc, d, ldh, ldw, vocab_offset, vocab, _ptr(labels),

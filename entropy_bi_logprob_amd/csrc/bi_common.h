@@ -30,6 +30,13 @@ bool aligned(const void* p, size_t a);
 int launched(const char* what);
 const char* last_error();
 
+// D[i][j] = sum_k A[i][k] B[j][k] (bf16 operands with rows of k contiguous
+// elements, fp32 accumulation; D fp32 or bf16) on the lm_head kernel's
+// matrix-core pipeline, queued on `stream`.  Used by the lm_head backward.
+int lmhead_product(const char* fn, const void* a, int64_t a_rows, int64_t lda, const void* b,
+                   int64_t b_rows, int64_t ldb, int64_t k, void* d, int64_t ldd, bool d_bf16,
+                   bi_stream_t stream);
+
 }  // namespace bi_internal
 
 namespace {

@@ -123,7 +123,13 @@ struct LmArgs {
   const float* token_weights;   // [n_tok] or NULL (= 1)
   uint16_t* gout;           // [n_voc, ldg] bf16 bits: gradient of the logits, vocabulary-major
   int64_t ldg;
+  void* dout;               // [n_voc, ldd] fp32 or bf16: the product itself (product kernel)
+  int64_t ldd;
+  int dout_bf16;
 };
+
+// What a workgroup does with its fp32 tile of D = W . H^T
+enum { kModeStats = 0, kModeGrad = 1, kModeProduct = 2 };
 
 // Tile (tv, tn) of linear tile index t: groups of kGroup token tiles sweep
 // the vocabulary tiles together.
@@ -188,14 +194,23 @@ struct LmFill {
   uint32_t lds0;       // this wave's first block: wave * 1 KB
 };
 
+// A pointer that is the same in every lane, marked so for the compiler (the
+// fill's scalar-base operand needs it in SGPRs).
+__device__ inline const char* uniform_ptr(const char* q) {
+  const uint64_t v = reinterpret_cast<uint64_t>(q);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
+  return reinterpret_cast<const char*>((uint64_t(hi) << 32) | lo);
+}
+
 __device__ inline LmFill lm_fill_setup(const LmArgs& p, int64_t v0, int64_t n0, int wave,
                                        int lane) {
   LmFill f;
   const int rb = lane / kChunks, slot = lane % kChunks;
   f.row0 = kBlockRows * wave + rb;
   f.cbytes = uint32_t(16 * (slot ^ lm_swz(f.row0)));   // lm_swz(row0 + 64 i) == lm_swz(row0)
-  f.wbase = reinterpret_cast<const char*>(p.weight + v0 * p.ldw);
-  f.hbase = reinterpret_cast<const char*>(p.hidden + n0 * p.ldh);
+  f.wbase = uniform_ptr(reinterpret_cast<const char*>(p.weight + v0 * p.ldw));
+  f.hbase = uniform_ptr(reinterpret_cast<const char*>(p.hidden + n0 * p.ldh));
   f.ldw2 = uint32_t(p.ldw * 2);
   f.ldh2 = uint32_t(p.ldh * 2);
   f.wlast = int(min(p.n_voc - v0, int64_t(kTV)) - 1);
@@ -393,11 +408,15 @@ __device__ inline void lm_stats_epilogue(const LmArgs& p, const f32x16 (&acc)[kX
   }
 }
 
-// GRAD = false: per-token statistics of each 256-row vocabulary tile.
-// GRAD = true:  the gradient of the logits, w * (softmax - onehot) from the
-// saved lse, written as bf16 (the cross-entropy backward of PR #4685
-// Summary, on the lm_head logits).  Same main loop, same logits bits.
-template <bool GRAD>
+// kModeStats:   per-token statistics of each 256-row vocabulary tile.
+// kModeGrad:    the gradient of the logits, w * (softmax - onehot) from the
+//               saved lse, written as bf16 (the cross-entropy backward of PR
+//               #4685 Summary, on the lm_head logits).
+// kModeProduct: the product itself, fp32 or bf16 (RNE), for the lm_head
+//               backward's G^T . hidden with the operands' roles taken by G
+//               and the transposed hidden states.
+// Same main loop, same product bits, in every mode.
+template <int MODE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEU, kWavesPerEU)))
 void lmhead_kernel(LmArgs p) {
   __shared__ __attribute__((aligned(1024))) char ring[kRingBytes];
@@ -417,8 +436,8 @@ void lmhead_kernel(LmArgs p) {
   for (int y = 0; y < kYB; ++y) {
     const int64_t j = n0 + kWN * wt + 32 * y + lr;
     const bool in = j < p.n_tok;
-    lab[y] = in ? p.labels[j] : p.ignore_index;
-    if constexpr (GRAD) {
+    if constexpr (MODE != kModeProduct) lab[y] = in ? p.labels[j] : p.ignore_index;
+    if constexpr (MODE == kModeGrad) {
       tlse[y] = in ? p.lse[j] : 0.0f;
       tw[y] = in && p.token_weights ? p.token_weights[j] : 1.0f;
     }
@@ -543,8 +562,26 @@ void lmhead_kernel(LmArgs p) {
   wait_counts<0, 15>();   // no request may still be writing LDS when the workgroup ends
   lds_barrier();          // every wave is done with the ring: the epilogues reuse it
 
-  const int64_t wrow0 = v0 + kWV * wv;     // first vocabulary row of this wave
-  if constexpr (GRAD) {
+  if constexpr (MODE == kModeProduct) {
+    // D[i][j] for the rows and columns that exist; for a given accumulator
+    // register the 64 lanes cover 32 consecutive columns of 2 rows
+#pragma unroll
+    for (int x = 0; x < kXB; ++x)
+#pragma unroll
+      for (int y = 0; y < kYB; ++y) {
+        const int64_t j = n0 + kWN * wt + 32 * y + lr;
+        if (j >= p.n_tok) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t i = v0 + kWV * wv + 32 * x + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (i >= p.n_voc) continue;
+          if (p.dout_bf16)
+            static_cast<__bf16*>(p.dout)[i * p.ldd + j] = __bf16(acc[x][y][r]);
+          else
+            static_cast<float*>(p.dout)[i * p.ldd + j] = acc[x][y][r];
+        }
+      }
+  } else if constexpr (MODE == kModeGrad) {
     // gradient of the logits: w * (p - [v == y]), p = 2^((z - lse) * log2e)
     // as the row backward computes it; +0 for ignored tokens, NaN for bad
     // labels.  The tile goes through LDS (the ring is free now) as bf16
@@ -600,12 +637,11 @@ void lmhead_kernel(LmArgs p) {
           dst[e] = uint16_t(w4[e >> 1] >> (16 * (e & 1)));
       }
     }
-    return;
+  } else {
+    typedef float Red[kWT][kYB][32][4];
+    static_assert(sizeof(Red) <= kRingBytes, "reduction fits the ring");
+    lm_stats_epilogue(p, acc, lab, tv, tn, wv, wt, lr, half, *reinterpret_cast<Red*>(ring));
   }
-
-  typedef float Red[kWT][kYB][32][4];
-  static_assert(sizeof(Red) <= kRingBytes, "reduction fits the ring");
-  lm_stats_epilogue(p, acc, lab, tv, tn, wv, wt, lr, half, *reinterpret_cast<Red*>(ring));
 }
 
 // Shared validation of the lm_head entry points; fills the common arguments.
@@ -648,17 +684,48 @@ int lm_setup(const char* fn, LmArgs* a, const void* hidden, const void* weight, 
   return BI_OK;
 }
 
-template <bool GRAD>
+template <int MODE>
 int lm_launch(const char* fn, const LmArgs& a, bi_stream_t stream) {
   const int64_t total = a.tiles_v * a.tiles_n;
   int64_t blocks = 8 * ((total + 7) / 8);
   if (blocks > 0x7fffffff) return fail(BI_ERR_SHAPE, "%s: too many tiles", fn);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(lmhead_kernel<GRAD>, dim3(unsigned(blocks)), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(lmhead_kernel<MODE>, dim3(unsigned(blocks)), dim3(kThreads), 0, s, a);
   return launched(fn);
 }
 
 }  // namespace
+
+namespace bi_internal {
+
+// D[i][j] = sum_k A[i][k] B[j][k] on the lm_head kernel's pipeline (A in the
+// lm_head rows' place, B in the hidden states'); k a multiple of kBK.
+int lmhead_product(const char* fn, const void* a, int64_t a_rows, int64_t lda, const void* b,
+                   int64_t b_rows, int64_t ldb, int64_t k, void* d, int64_t ldd, bool d_bf16,
+                   bi_stream_t stream) {
+  if (k < kBK || k % kBK != 0 || k > (int64_t(1) << 22) || lda < k || ldb < k || lda % 8 ||
+      ldb % 8 || lda > (int64_t(1) << 22) || ldb > (int64_t(1) << 22) || ldd < b_rows)
+    return fail(BI_ERR_SHAPE, "%s: product shape outside the kernel's limits", fn);
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(d, d_bf16 ? 2 : 4))
+    return fail(BI_ERR_ALIGN, "%s: misaligned product operand", fn);
+  if (a_rows == 0 || b_rows == 0) return BI_OK;
+  LmArgs p{};
+  p.weight = static_cast<const uint16_t*>(a);
+  p.hidden = static_cast<const uint16_t*>(b);
+  p.n_voc = a_rows;
+  p.n_tok = b_rows;
+  p.d = k;
+  p.ldw = lda;
+  p.ldh = ldb;
+  p.dout = d;
+  p.ldd = ldd;
+  p.dout_bf16 = d_bf16 ? 1 : 0;
+  p.tiles_v = (a_rows + kTV - 1) / kTV;
+  p.tiles_n = (b_rows + kTN - 1) / kTN;
+  return lm_launch<kModeProduct>(fn, p, stream);
+}
+
+}  // namespace bi_internal
 
 extern "C" {
 
@@ -682,7 +749,7 @@ int bi_lmhead_tile_stats(const void* hidden, const void* weight, int64_t n_token
   if (!stats) return fail(BI_ERR_NULL, "%s: stats is required", fn);
   if (!aligned(stats, 16)) return fail(BI_ERR_ALIGN, "%s: stats needs 16-byte alignment", fn);
   a.stats = stats;
-  return lm_launch<false>(fn, a, stream);
+  return lm_launch<kModeStats>(fn, a, stream);
 }
 
 int bi_lmhead_grad_logits(const void* hidden, const void* weight, int64_t n_tokens,
@@ -707,7 +774,7 @@ int bi_lmhead_grad_logits(const void* hidden, const void* weight, int64_t n_toke
   a.token_weights = token_weights;
   a.gout = static_cast<uint16_t*>(grad_logits);
   a.ldg = grad_stride;
-  return lm_launch<true>(fn, a, stream);
+  return lm_launch<kModeGrad>(fn, a, stream);
 }
 
 }  // extern "C"

@@ -13,14 +13,19 @@
 // How: the vocabulary shard is cut into chunks of rows that fit the caller's
 // workspace.  For each chunk, bi_lmhead_grad_logits recomputes its logits on
 // the matrix cores (the forward's exact MFMA sequence) and writes G for the
-// chunk as bf16, vocabulary-major [rows][n_tokens]; then two plain library
-// GEMMs (hipBLASLt, bf16 operands, fp32 accumulation) add G @ W_chunk into
-// grad_hidden and write G^T @ hidden into the chunk's grad_weight rows.  All
-// of it is queued on the caller's stream; hipBLASLt works in the first part
-// of the caller's workspace, so nothing here allocates device memory except
-// the per-device hipBLASLt handle, created on the first call on a device.
-// The algorithm of each GEMM shape is chosen once by hipBLASLt's heuristic
-// and kept, so a shape always runs the same kernel (reproducible results).
+// chunk as bf16, vocabulary-major [rows][n_tokens]; then G @ W_chunk is added
+// into grad_hidden by a plain library GEMM (hipBLASLt, bf16 operands, fp32
+// accumulation), and G^T @ hidden is written into the chunk's grad_weight
+// rows.  That second product has G's rows, token-contiguous, as one operand:
+// when n_tokens is a multiple of 64 (at most 2^22) and the workspace holds a
+// transposed copy of the hidden states ([d][n_tokens], made once per call),
+// it runs on the lm_head kernel's own matrix-core pipeline, otherwise on
+// hipBLASLt too.  All of it is queued on the caller's stream; hipBLASLt
+// works in the first part of the caller's workspace, so nothing here
+// allocates device memory except the per-device hipBLASLt handle, created on
+// the first call on a device.  The algorithm of each library GEMM shape is
+// chosen once by hipBLASLt's heuristic and kept, so a shape always runs the
+// same kernel (reproducible results).
 
 #include <hip/hip_runtime.h>
 #include <hipblaslt/hipblaslt.h>
@@ -41,6 +46,45 @@ constexpr int kMaxDevices = 64;
 
 // token stride of the grad-logits chunk: rows start on 16-byte boundaries
 int64_t grad_ld(int64_t n_tokens) { return (n_tokens + 7) / 8 * 8; }
+
+// G^T @ hidden on the matrix-core pipeline needs the token count to be a
+// whole number of its 64-wide K stages (and within its 2^22 limit)
+bool own_product(int64_t n_tokens) {
+  return n_tokens % 64 == 0 && n_tokens <= (int64_t(1) << 22);
+}
+
+// bytes of the transposed hidden states [d][n_tokens] in the workspace
+int64_t transposed_bytes(int64_t n_tokens, int64_t d) {
+  return own_product(n_tokens) ? (d * n_tokens * 2 + 255) / 256 * 256 : 0;
+}
+
+// ht[c][n] = h[n][c] for a 64 x 64 block per workgroup (n_tokens and d are
+// multiples of 64, rows 16-byte aligned): 16-byte loads, a padded LDS tile,
+// 16-byte stores.
+constexpr int kTp = 64;
+__global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restrict__ h,
+                                                         int64_t ldh, uint16_t* __restrict__ ht,
+                                                         int64_t ldht) {
+  __shared__ uint16_t tile[kTp][kTp + 8];
+  const int64_t n0 = int64_t(blockIdx.x) * kTp, c0 = int64_t(blockIdx.y) * kTp;
+  for (int q = threadIdx.x; q < kTp * kTp / 8; q += 256) {
+    const int n = q / (kTp / 8), cc = 8 * (q % (kTp / 8));
+    const u32x4 v = *reinterpret_cast<const u32x4*>(h + (n0 + n) * ldh + c0 + cc);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) tile[cc + e][n] = uint16_t(w[e >> 1] >> (16 * (e & 1)));
+  }
+  __syncthreads();
+  for (int q = threadIdx.x; q < kTp * kTp / 8; q += 256) {
+    const int c = q / (kTp / 8), nn = 8 * (q % (kTp / 8));
+    u32x4 v;
+    v.x = uint32_t(tile[c][nn + 0]) | (uint32_t(tile[c][nn + 1]) << 16);
+    v.y = uint32_t(tile[c][nn + 2]) | (uint32_t(tile[c][nn + 3]) << 16);
+    v.z = uint32_t(tile[c][nn + 4]) | (uint32_t(tile[c][nn + 5]) << 16);
+    v.w = uint32_t(tile[c][nn + 6]) | (uint32_t(tile[c][nn + 7]) << 16);
+    *reinterpret_cast<u32x4*>(ht + (c0 + c) * ldht + n0 + nn) = v;
+  }
+}
 
 std::mutex g_blas_mutex;
 hipblasLtHandle_t g_lt[kMaxDevices];
@@ -151,10 +195,10 @@ int lt_gemm(const char* fn, hipblasLtHandle_t h, int dev, const Gemm& g, const v
 
 extern "C" {
 
-int64_t bi_lmhead_backward_workspace(int64_t n_tokens, int64_t chunk_rows) {
-  if (n_tokens < 0 || chunk_rows < 1) return -1;
+int64_t bi_lmhead_backward_workspace(int64_t n_tokens, int64_t d, int64_t chunk_rows) {
+  if (n_tokens < 0 || d < 0 || chunk_rows < 1) return -1;
   const int64_t rows = (chunk_rows + kChunkAlign - 1) / kChunkAlign * kChunkAlign;
-  return kBlasWorkspace + rows * grad_ld(n_tokens) * 2;
+  return kBlasWorkspace + transposed_bytes(n_tokens, d) + rows * grad_ld(n_tokens) * 2;
 }
 
 int bi_lmhead_backward(const void* hidden, const void* weight, int64_t n_tokens,
@@ -184,15 +228,22 @@ int bi_lmhead_backward(const void* hidden, const void* weight, int64_t n_tokens,
       !aligned(workspace, 256))
     return fail(BI_ERR_ALIGN, "%s: misaligned pointer (workspace needs 256 bytes)", fn);
   const int64_t ldg = grad_ld(n_tokens);
-  const int64_t fit = workspace_bytes > kBlasWorkspace
-                          ? (workspace_bytes - kBlasWorkspace) / (ldg * 2) / kChunkAlign * kChunkAlign
-                          : 0;
+  // the transposed hidden states when G^T @ hidden can run on the matrix-core
+  // pipeline and the workspace holds them beside one chunk; else the library
+  int64_t ht_bytes = transposed_bytes(n_tokens, d);
+  if (workspace_bytes < kBlasWorkspace + ht_bytes + kChunkAlign * ldg * 2) ht_bytes = 0;
+  const bool own = ht_bytes > 0;
+  const int64_t room = workspace_bytes - kBlasWorkspace - ht_bytes;
+  const int64_t fit = room > 0 ? room / (ldg * 2) / kChunkAlign * kChunkAlign : 0;
   const int64_t chunk = fit < n_vocab_rows ? fit : n_vocab_rows;
   if (chunk < 1)
     return fail(BI_ERR_SHAPE, "%s: workspace of %lld bytes is below %lld", fn,
                 (long long)workspace_bytes,
-                (long long)bi_lmhead_backward_workspace(n_tokens, kChunkAlign));
-  uint16_t* g = reinterpret_cast<uint16_t*>(static_cast<char*>(workspace) + kBlasWorkspace);
+                (long long)(bi_lmhead_backward_workspace(n_tokens, d, kChunkAlign) -
+                            transposed_bytes(n_tokens, d)));
+  char* ws = static_cast<char*>(workspace);
+  uint16_t* ht = reinterpret_cast<uint16_t*>(ws + kBlasWorkspace);
+  uint16_t* g = reinterpret_cast<uint16_t*>(ws + kBlasWorkspace + ht_bytes);
   const size_t gw_elem = grad_weight_dtype == BI_BF16 ? 2 : 4;
 
   std::lock_guard<std::mutex> lock(g_blas_mutex);
@@ -201,6 +252,14 @@ int bi_lmhead_backward(const void* hidden, const void* weight, int64_t n_tokens,
   if (int r = lt_handle(fn, &dev, &h)) return r;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const hipDataType gw_type = grad_weight_dtype == BI_BF16 ? HIP_R_16BF : HIP_R_32F;
+  if (own) {
+    if (d % kTp != 0 || !aligned(hidden, 16) || hidden_stride % 8 != 0)
+      return fail(BI_ERR_SHAPE, "%s: d must be a multiple of 64 with 16-byte hidden rows", fn);
+    hipLaunchKernelGGL(transpose_kernel, dim3(unsigned(n_tokens / kTp), unsigned(d / kTp)),
+                       dim3(256), 0, s, static_cast<const uint16_t*>(hidden), hidden_stride, ht,
+                       n_tokens);
+    if (int r = launched(fn)) return r;
+  }
   for (int64_t c0 = 0; c0 < n_vocab_rows; c0 += chunk) {
     const int64_t rows = n_vocab_rows - c0 < chunk ? n_vocab_rows - c0 : chunk;
     const uint16_t* wc = static_cast<const uint16_t*>(weight) + c0 * weight_stride;
@@ -215,13 +274,20 @@ int bi_lmhead_backward(const void* hidden, const void* weight, int64_t n_tokens,
     if (int r = lt_gemm(fn, h, dev, dh, wc, g, 1.0f, grad_hidden, workspace,
                         size_t(kBlasWorkspace), s))
       return r;
-    // grad_weight_c^T (d x rows) = hidden^T (d x N) . G (N x rows)
     void* gwc = static_cast<char*>(grad_weight) + c0 * grad_weight_stride * int64_t(gw_elem);
-    const Gemm dw{HIPBLAS_OP_N, HIPBLAS_OP_N, d, rows, n_tokens, hidden_stride, ldg,
-                  grad_weight_stride, gw_type};
-    if (int r = lt_gemm(fn, h, dev, dw, hidden, g, 0.0f, gwc, workspace, size_t(kBlasWorkspace),
-                        s))
-      return r;
+    if (own) {
+      // grad_weight_c[v][c] = sum_n G[v][n] ht[c][n]
+      if (int r = lmhead_product(fn, g, rows, ldg, ht, d, n_tokens, n_tokens, gwc,
+                                 grad_weight_stride, grad_weight_dtype == BI_BF16, stream))
+        return r;
+    } else {
+      // grad_weight_c^T (d x rows) = hidden^T (d x N) . G (N x rows)
+      const Gemm dw{HIPBLAS_OP_N, HIPBLAS_OP_N, d, rows, n_tokens, hidden_stride, ldg,
+                    grad_weight_stride, gw_type};
+      if (int r = lt_gemm(fn, h, dev, dw, hidden, g, 0.0f, gwc, workspace,
+                          size_t(kBlasWorkspace), s))
+        return r;
+    }
   }
   return launched(fn);
 }

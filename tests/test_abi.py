@@ -191,9 +191,11 @@ def test_lmhead_grad_logits_argument_errors(L):
 def test_lmhead_backward_argument_errors(L):
     f = L.bi_lmhead_backward
     ws = L.bi_lmhead_backward_workspace
-    need = ws(8, 256)
-    assert need == (128 << 20) + 256 * 8 * 2 and ws(9, 1) == (128 << 20) + 256 * 16 * 2
-    assert ws(-1, 256) == -1 and ws(8, 0) == -1
+    need = ws(8, 128, 256)
+    assert need == (128 << 20) + 256 * 8 * 2 and ws(9, 128, 1) == (128 << 20) + 256 * 16 * 2
+    # 64 tokens: room for the transposed hidden states too
+    assert ws(64, 128, 256) == (128 << 20) + 128 * 64 * 2 + 256 * 64 * 2
+    assert ws(-1, 128, 256) == -1 and ws(8, 128, 0) == -1 and ws(8, -1, 256) == -1
     args = dict(h=P, w=P, n=8, vc=300, d=128, ldh=128, ldw=128, off=0, v=300, lab=P, lse=P,
                 gh=P, ldgh=128, gw=P, gdt=bi.BI_BF16, ldgw=128, ws=ctypes.c_void_p(0x100000),
                 wsb=need)

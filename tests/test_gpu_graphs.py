@@ -113,14 +113,14 @@ def test_lmhead_statistics_replay():
 def test_lmhead_backward_replays():
     # grad-logits kernel plus two library GEMMs per vocabulary chunk; the
     # workspace and the outputs are the caller's, so the graph owns nothing
-    n, vc, d, chunk = 300, 1000, 128, 256
+    n, vc, d, chunk = 320, 1000, 128, 256   # 320 tokens: the matrix-core G^T . hidden
     b = wl.lmhead_batch(n, vc, d, seed=45, ignore_frac=0.05)
     to_bf16 = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda() \
         .view(torch.bfloat16)
     H, W, y = to_bf16(b.hidden), to_bf16(b.weight), dev(b.labels)
     _, _, lse = bi.lmhead_logprob(H, W, y)
     tw = torch.linspace(-1.0, 1.0, n, device="cuda")
-    ws = torch.empty(int(bi.lib().bi_lmhead_backward_workspace(n, chunk)), dtype=torch.uint8,
+    ws = torch.empty(int(bi.lib().bi_lmhead_backward_workspace(n, d, chunk)), dtype=torch.uint8,
                      device="cuda")
     gh = torch.zeros((n, d), device="cuda")
     gw = torch.empty((vc, d), dtype=torch.bfloat16, device="cuda")

@@ -232,6 +232,30 @@ def test_backward_against_oracle(n, vc, d, chunk, gdt):
     _check_grads(host(gh), host(gw.float()), G, h, w, gdt == torch.bfloat16)
 
 
+@pytest.mark.parametrize("n,vc,d,chunk,pad", [(256, 1000, 128, 256, 0), (640, 1030, 192, 512, 0),
+                                              (256, 700, 128, 512, 64)])
+@pytest.mark.parametrize("gdt", [torch.float32, torch.bfloat16], ids=["gw_f32", "gw_bf16"])
+def test_backward_with_the_matrix_core_product(n, vc, d, chunk, pad, gdt):
+    # n_tokens a multiple of 64: G^T @ hidden runs on the lm_head kernel from
+    # the transposed hidden states; with a workspace one byte short of that
+    # copy plus one 256-row chunk the library takes it; both meet the bound
+    b, H, W, labels, h, w, olse, tw = _setup(n, vc, d, seed=n + d + pad)
+    if pad:
+        H = _padded(H, pad)
+    lse, lse_o = _saved_lse(olse)
+    G = orc.lmhead_backward(h, w, b.labels, lse_o, tw)
+    need = int(bi.lib().bi_lmhead_backward_workspace(n, d, chunk))
+    copy = need - (128 << 20) - chunk * n * 2          # the transposed hidden states
+    assert copy >= n * d * 2
+    short = (128 << 20) + copy + 256 * n * 2 - 1
+    for wsb in (need, short):
+        ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+        gh, gw = bi.lmhead_backward(H, W, labels, lse, dev(tw), grad_weight_dtype=gdt,
+                                    chunk_rows=chunk, workspace=ws)
+        torch.cuda.synchronize()
+        _check_grads(host(gh), host(gw.float()), G, h, w, gdt == torch.bfloat16)
+
+
 def _padded(t, extra):
     # the same values in rows `extra` elements longer (a column slice of a wider buffer)
     wide = torch.zeros((t.shape[0], t.shape[1] + extra), dtype=t.dtype, device=t.device)
