@@ -13,7 +13,7 @@ import workloads as wl
 from gpu_util import dev, dev_logits
 
 pytestmark = pytest.mark.gpu
-ROUNDS = 4
+REPEATS = 4
 
 
 def to_bf16(bits):
@@ -52,12 +52,12 @@ def test_two_threads_two_streams():
             s = torch.cuda.Stream()
             with torch.cuda.stream(s):
                 barrier.wait(timeout=60)
-                for r in range(ROUNDS):
+                for r in range(REPEATS):
                     outs = run(cases[i])
                     s.synchronize()
                     for k, (o, ref) in enumerate(zip(outs, refs[i])):
                         if not same(o, ref):
-                            errors.append(f"thread {i}, round {r}, output {k} differs")
+                            errors.append(f"thread {i}, repeat {r}, output {k} differs")
         except Exception as e:  # reported below, with the thread that raised it
             errors.append(f"thread {i}: {e!r}")
 
