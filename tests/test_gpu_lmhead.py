@@ -332,3 +332,70 @@ def test_autograd_through_the_lm_head():
     assert_close(host(lp.detach()), olp, TOL, "logprob")
     assert_close(host(ent), oent, TOL, "entropy")
 
+
+
+# ---- the full-size lm_head step, sampled
+
+def _vocab_columns_backward(h, w, labels, lse, tw, cols):
+    """Columns `cols` of G = w (softmax - onehot) and the grad_weight rows
+    G[:, cols]^T @ hidden, from the oracle's logits and backward.  The
+    softmax of a column needs only its logit and the row's saved lse; one
+    extra column at -inf takes the onehot of every label outside `cols`
+    (its probability is exactly 0), so the kept columns are the full
+    matrix's."""
+    z = np.concatenate([orc.lmhead_logits(h, w[cols]), np.full((h.shape[0], 1), -np.inf)], axis=1)
+    pos = {int(c): i for i, c in enumerate(cols)}
+    lab = np.array([pos.get(int(y), len(cols)) if y != -100 else -100 for y in labels])
+    G = orc.backward(z, lab, lse, tw)[:, :len(cols)]
+    return G, G.T @ h
+
+
+@pytest.mark.timeout(900)
+def test_bench_shape_sampled():
+    # 32768 tokens, the Qwen3 vocabulary, hidden size 2560: the statistics and
+    # the backward launched as the throughput benchmark launches them (one
+    # 32768-row chunk, a mean over tokens, grad_weight in bf16, the product on
+    # the lm_head kernel).  A grad_hidden row needs the token's whole logit
+    # row, a grad_weight row one logit column over every token: the oracle
+    # checks sampled tokens and sampled vocabulary rows (both tile edges, the
+    # ragged last tile, and the labels of sampled tokens for the onehot term).
+    n, vc, d = 32768, wl.QWEN3_VOCAB, wl.LMHEAD_HIDDEN
+    b = wl.lmhead_batch(n, vc, d, seed=19)
+    H, W, labels = to_dev_bf16(b.hidden), to_dev_bf16(b.weight), dev(b.labels)
+    lp, ent, lse = bi.lmhead_logprob(H, W, labels)
+    h, w = orc.decode(b.hidden, "bf16"), orc.decode(b.weight, "bf16")
+    # the saved lse, a seeded stand-in near each row's normaliser: the logits
+    # of these inputs are Gaussian with variance 4 |h|^2 / d, so sum exp(z)
+    # is about vc exp(2 |h|^2 / d)
+    lse32 = (np.log(vc) + 2.0 * np.mean(h * h, axis=1)).astype(np.float32)
+    lse_o = lse32.astype(np.float64)
+    tw = np.full(n, -1.0 / n, dtype=np.float32)
+    ws = torch.empty(int(bi.lib().bi_lmhead_backward_workspace(n, d, n)), dtype=torch.uint8,
+                     device="cuda")
+    gh = torch.zeros((n, d), dtype=torch.float32, device="cuda")
+    gw = torch.empty((vc, d), dtype=torch.bfloat16, device="cuda")
+    bi.lmhead_backward(H, W, labels, dev(lse32), dev(tw), grad_hidden=gh, grad_weight=gw,
+                       chunk_rows=n, workspace=ws)
+    torch.cuda.synchronize()
+    del ws
+
+    rng = np.random.default_rng(20)
+    rows = np.array(sorted({0, 1, n - 1, *rng.choice(n, 13, replace=False)}))
+    olp, oent, olse = orc.forward(orc.lmhead_logits(h[rows], w), b.labels[rows])
+    assert_close(host(lp)[rows], olp, TOL, "logprob")
+    assert_close(host(ent)[rows], oent, TOL, "entropy")
+    assert_close(host(lse)[rows], olse, TOL, "lse")
+
+    G, oh, _ = orc.lmhead_backward(h[rows], w, b.labels[rows], lse_o[rows], tw[rows])
+    bh = (2.0 ** -8 + vc * 2.0 ** -24) * (np.abs(G) @ np.abs(w)) + 1e-7
+    eh = np.abs(host(gh)[rows] - oh)
+    assert np.all(eh <= bh), float(np.max(eh - bh))
+
+    last = vc - vc % 256 if vc % 256 else vc - 256
+    cols = np.array(sorted({0, 255, 256, last - 1, last, vc - 1,
+                            *b.labels[rows[:6]], *rng.choice(vc, 6, replace=False)}))
+    G, ow = _vocab_columns_backward(h, w, b.labels, lse_o, tw, cols)
+    assert np.count_nonzero(np.isin(b.labels, cols)) >= 6
+    bw = (2.0 ** -8 + n * 2.0 ** -24) * (np.abs(G).T @ np.abs(h)) + 1e-7 + 0.5 * ulp_bf16(ow)
+    ew = np.abs(host(gw[torch.from_numpy(cols).cuda()].float()) - ow)
+    assert np.all(ew <= bw), float(np.max(ew - bw))
