@@ -325,14 +325,26 @@ __device__ inline void lm_merge(Acc& a, float& ta, const Acc& b, float tb) {
 // Statistics of each token over one tile's 256 vocabulary rows, written as
 // the tile's bi_stats (fixed order: the lane's values, the lane halves, the
 // two vocabulary waves).
-__device__ inline void lm_stats_epilogue(const LmArgs& p, const f32x16 (&acc)[kXB][kYB],
+__device__ inline void lm_stats_epilogue(const LmArgs& p, f32x16 (&acc)[kXB][kYB],
                                          const int64_t (&lab)[kYB], int64_t tv, int64_t tn,
                                          int wv, int wt, int lr, int half,
                                          float (&red)[kWT][kYB][32][4]) {
   const int64_t v0 = tv * kTV, n0 = tn * kTN;
   const int64_t wrow0 = v0 + kWV * wv;     // first vocabulary row of this wave
-  // rows of this wave that exist (uniform); the others are masked to -inf
+  // rows of this wave that exist (uniform); on the ragged last tile the
+  // others are masked to -inf first, so that full tiles select nothing
   const int valid = int(max(int64_t(0), min(p.n_voc - wrow0, int64_t(kWV))));
+  if (valid < kWV) {
+#pragma unroll
+    for (int x = 0; x < kXB; ++x)
+#pragma unroll
+      for (int y = 0; y < kYB; ++y)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = 32 * x + 8 * (r >> 2) + 4 * half + (r & 3);   // within the wave
+          if (row >= valid) acc[x][y][r] = -INFINITY;
+        }
+  }
   float tl[kYB];
   Acc lo[kYB];
 #pragma unroll
@@ -341,10 +353,7 @@ __device__ inline void lm_stats_epilogue(const LmArgs& p, const f32x16 (&acc)[kX
 #pragma unroll
     for (int x = 0; x < kXB; ++x)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = 32 * x + 8 * (r >> 2) + 4 * half + (r & 3);   // within the wave
-        z[16 * x + r] = row < valid ? acc[x][y][r] : -INFINITY;
-      }
+      for (int r = 0; r < 16; ++r) z[16 * x + r] = acc[x][y][r];
     Acc a = acc_empty();
     accumulate<8, 2 * kXB>(a, z);
     // the label's logit, held by exactly one lane of one vocabulary wave (if
@@ -406,6 +415,22 @@ __device__ inline void lm_stats_epilogue(const LmArgs& p, const f32x16 (&acc)[kX
       }
     }
   }
+}
+
+// Byte offset of (vocabulary row, token) in the gradient epilogue's LDS tile,
+// bf16 [kTV][kTN]: the 16-byte chunks of a row are XOR-swizzled by 4 * (row
+// bit 0 + 2 * row bit 2), so the rows r, r+1, r+4, r+5 that one 4-byte write
+// instruction covers land on disjoint banks.
+__device__ inline int lm_grad_at(int row, int tok) {
+  const int key = ((row & 1) | ((row >> 1) & 2)) << 2;
+  return row * (kTN * 2) + (((tok >> 3) ^ key) << 4) + ((tok & 7) << 1);
+}
+
+// two floats as bf16 (round to nearest even), `lo` in the low half
+__device__ inline uint32_t pack_bf16(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t v = {__bf16(lo), __bf16(hi)};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // kModeStats:   per-token statistics of each 256-row vocabulary tile.
@@ -585,34 +610,68 @@ void lmhead_kernel(LmArgs p) {
     // gradient of the logits: w * (p - [v == y]), p = 2^((z - lse) * log2e)
     // as the row backward computes it; +0 for ignored tokens, NaN for bad
     // labels.  The tile goes through LDS (the ring is free now) as bf16
-    // [vocab row][token], 16-byte chunks of a row XOR-swizzled by the row, so
-    // that it leaves as whole 16-byte vectors of 8 tokens: vocabulary-major.
+    // [vocab row][token], so that it leaves as whole 16-byte vectors of 8
+    // tokens: vocabulary-major.  A lane holds 4 consecutive rows of one
+    // token; neighbouring lanes (tokens t, t+1) swap halves of their packed
+    // row pairs, so each lane writes 4-byte words of two tokens (even lane:
+    // rows 0 and 2 of the four, odd lane: rows 1 and 3).  16-byte chunks of a
+    // row are XOR-swizzled by row bits 0 and 2, which makes the four rows of
+    // one write instruction fall on different banks.  Every element is
+    // written as w * p first; the label's element, w * (p - 1), afterwards by
+    // the lane holding its logit (same wave, so in order).
     static_assert(kTV * kTN * 2 <= kRingBytes, "grad tile fits the ring");
-    constexpr int kTileRowBytes = kTN * 2;
+    const int odd = lr & 1;
+    const uint32_t sel = odd ? 0x03020706u : 0x05040100u;   // v_perm: see below
 #pragma unroll
     for (int y = 0; y < kYB; ++y) {
       const int tok = kWN * wt + 32 * y + lr;   // token within the tile
-      const int64_t j = n0 + tok;
-      if (j >= p.n_tok) continue;
-      const int64_t lb = lab[y];
+      const int64_t lb = lab[y];                // tokens past the end: ignored, never stored
       const bool ignored = lb == p.ignore_index;
       const bool bad = !ignored && (lb < 0 || lb >= p.vocab);
       const float lse = tlse[y];
-      const float w = tw[y];
-      // the label's row within this tile, or -1
-      const int64_t yl = lb - p.vocab_offset - v0;
-      const int ylr = yl >= 0 && yl < kTV ? int(yl) : -1;
+      const float wg = bad ? NAN : tw[y];
+      // halves of a packed word belong to tokens tp and tp+1: keep each one
+      // unless its token is ignored (+0 whatever its logits)
+      const uint32_t keep = ignored ? 0u : 0xffffu;
+      const uint32_t keep_nb = uint32_t(__builtin_amdgcn_mov_dpp(int(keep), 0xB1, 0xF, 0xF, true));
+      const uint32_t mask = odd ? (keep_nb | (keep << 16)) : (keep | (keep_nb << 16));
+      const int tp = tok & ~1;
 #pragma unroll
       for (int x = 0; x < kXB; ++x)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = kWV * wv + 32 * x + 8 * (r >> 2) + 4 * half + (r & 3);
-          const float pr = exp2_hw((acc[x][y][r] - lse) * kLog2e);
-          float g = row == ylr ? w * (pr - 1.0f) : w * pr;
-          g = ignored ? 0.0f : (bad ? NAN : g);
-          const int at = row * kTileRowBytes + ((((tok >> 3) ^ (row & 31)) << 4) | ((tok & 7) << 1));
-          *reinterpret_cast<__bf16*>(ring + at) = __bf16(g);
+        for (int g = 0; g < 4; ++g) {
+          float gv[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) gv[i] = wg * exp2_hw((acc[x][y][4 * g + i] - lse) * kLog2e);
+          // rows r0..r3 of token t packed in pairs (low half the lower row)
+          const uint32_t p01 = pack_bf16(gv[0], gv[1]), p23 = pack_bf16(gv[2], gv[3]);
+          // the neighbour's (token t ^ 1), by a quad permutation [1, 0, 3, 2]
+          const uint32_t q01 = uint32_t(__builtin_amdgcn_mov_dpp(int(p01), 0xB1, 0xF, 0xF, true));
+          const uint32_t q23 = uint32_t(__builtin_amdgcn_mov_dpp(int(p23), 0xB1, 0xF, 0xF, true));
+          // v_perm picks bytes of {q (bytes 4-7), p (bytes 0-3)}: an even lane
+          // keeps the low halves (its row r0 / r2: tokens t, t+1), an odd lane
+          // the high ones (r1 / r3: tokens t-1, t)
+          const uint32_t a = __builtin_amdgcn_perm(q01, p01, sel) & mask;
+          const uint32_t b = __builtin_amdgcn_perm(q23, p23, sel) & mask;
+          const int row = kWV * wv + 32 * x + 8 * g + 4 * half + odd;
+          *reinterpret_cast<uint32_t*>(ring + lm_grad_at(row, tp)) = a;
+          *reinterpret_cast<uint32_t*>(ring + lm_grad_at(row + 2, tp)) = b;
         }
+      // the label's element, if this wave holds it: the select chain runs
+      // only when some lane of the wave needs it
+      const int64_t yl = lb - p.vocab_offset - v0 - kWV * wv;   // row within this wave's 128
+      const bool mine = !ignored && !bad && yl >= 0 && yl < kWV && half == ((yl >> 2) & 1);
+      if (__builtin_amdgcn_ballot_w64(mine)) {
+        const int q = mine ? int(yl >> 5) * 16 + int((yl & 31) >> 3) * 4 + int(yl & 3) : -1;
+        float z = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 16 * kXB; ++k) z = q == k ? acc[k / 16][y][k % 16] : z;
+        if (mine) {
+          const float pr = exp2_hw((z - lse) * kLog2e);
+          *reinterpret_cast<__bf16*>(ring + lm_grad_at(kWV * wv + int(yl), tok)) =
+              __bf16(tw[y] * (pr - 1.0f));
+        }
+      }
       if (bad && p.status_flag && tv == 0 && wv == 0 && half == 0)
         atomicOr(p.status_flag, BI_FLAG_BAD_LABEL);
     }
@@ -626,8 +685,7 @@ void lmhead_kernel(LmArgs p) {
       const int row = q / kChunksPerRow, c = q % kChunksPerRow;
       const int64_t i = v0 + row, j0 = n0 + 8 * c;
       if (i >= p.n_voc || j0 >= p.n_tok) continue;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(
-          ring + row * kTileRowBytes + ((c ^ (row & 31)) << 4));
+      const u32x4 v = *reinterpret_cast<const u32x4*>(ring + lm_grad_at(row, 8 * c));
       uint16_t* dst = p.gout + i * p.ldg + j0;
       if (vec && j0 + 8 <= p.n_tok) {
         *reinterpret_cast<u32x4*>(dst) = v;
