@@ -204,6 +204,35 @@ def test_grad_logits_bad_label_is_nan_and_flagged():
     assert np.isnan(gf[:, 3]).all() and np.isfinite(np.delete(gf, 3, axis=1)).all()
 
 
+def test_ignore_index_that_is_a_vocabulary_row():
+    # ignore_index 7 is also a row of the lm_head: tokens labelled 7 are
+    # ignored (logprob and gradient +0, no onehot term at row 7), and row 7
+    # still gets every other token's softmax term
+    n, vc, d, ii = 300, 700, 128, 7
+    b, H, W, _, h, w, olse, tw = _setup(n, vc, d, seed=31, ignore_frac=0.0)
+    lab = np.where(b.labels == ii, ii + 1, b.labels)
+    lab[np.random.default_rng(3).choice(n, 40, replace=False)] = ii
+    ign = lab == ii
+    lp, ent, lse = bi.lmhead_logprob(H, W, dev(lab), ignore_index=ii)
+    torch.cuda.synchronize()
+    olp, oent, olse2 = orc.forward(orc.lmhead_logits(h, w), lab, ignore_index=ii)
+    assert_close(host(lp), olp, TOL, "logprob")
+    assert_close(host(ent), oent, TOL, "entropy")
+    assert_close(host(lse), olse2, TOL, "lse")
+    assert np.all(host(lp)[ign] == 0) and not np.any(np.signbit(host(lp)[ign]))
+    lse_d, lse_o = _saved_lse(olse)
+    g = bi.lmhead_grad_logits(H, W, dev(lab), lse_d, dev(tw), ignore_index=ii)
+    gh, gw = bi.lmhead_backward(H, W, dev(lab), lse_d, dev(tw), ignore_index=ii,
+                                grad_weight_dtype=torch.float32)
+    torch.cuda.synchronize()
+    G = orc.lmhead_backward(h, w, lab, lse_o, tw, ignore_index=ii)
+    got = orc.decode(host(g.view(torch.int16)).view(np.uint16), "bf16").T   # [n, vc]
+    bound = 1e-5 * np.abs(tw)[:, None] + ulp_bf16(G[0])
+    assert np.all(np.abs(got - G[0]) <= bound), float(np.max(np.abs(got - G[0]) - bound))
+    assert np.all(got[ign] == 0) and not np.any(np.signbit(got[ign]))
+    _check_grads(host(gh), host(gw), G, h, w, False)
+
+
 def _check_grads(gh, gw, G, h, w, gw_bf16):
     """|error| within bf16 rounding of G (2^-9 relative) plus fp32 accumulation,
     bounded through the absolute products: (2^-8 + K 2^-24) |G| @ |operand|."""

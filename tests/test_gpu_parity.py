@@ -423,3 +423,42 @@ def test_trainer_and_generator_logprobs_are_bitwise_equal():
     rows = torch.arange(0, 512, 37, device="cuda")
     stats = host(bi.diff_stats(pi[rows].contiguous(), mu[rows].contiguous(), labels[rows].contiguous()))
     assert np.all(stats == 0), stats
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_ignore_index_that_is_a_column(dt):
+    # ignore_index 3 is also a valid column: rows labelled 3 are ignored (+0
+    # logprob and gradient, entropy kept) on every path that takes a label, and
+    # column 3 still gets the softmax term of every other row
+    ii, n, v = 3, 37, 5_003
+    b = random_batch(n, v, dt, seed=91, ignore_frac=0.0)
+    lab = np.where(b.labels == ii, ii + 1, b.labels)
+    lab[np.random.default_rng(5).choice(n, 9, replace=False)] = ii
+    ign = lab == ii
+    tl, te, tg = TOL[dt]
+    z = orc.decode(b.logits, dt)
+    olp, oent, olse = orc.forward(z, lab, ignore_index=ii)
+    og = orc.backward(z, lab, olse, b.weights, ignore_index=ii)
+    logits, labels, w = dev_logits(b.logits, dt), dev(lab), dev(b.weights)
+    lp, ent, lse = bi.fwd(logits, labels, ii)
+    g = bi.bwd(logits, labels, lse, w, torch.float32, ii)
+    flp, fent, flse, fg = bi.fwd_bwd(logits, labels, w, torch.float32, ii)
+    bounds = [(0, 2000), (2000, 2001), (2001, v)]
+    st = torch.stack([bi.vocab_chunk_stats(logits[:, a:c], labels, a, v, ii) for a, c in bounds])
+    clp, cent, clse = bi.stats_combine(st, labels, ii)
+    mlab = torch.stack([labels, torch.full_like(labels, ii), (labels + 1) % v], dim=1)
+    mlp, ment, mlse = bi.fwd_multi(logits, mlab, ii)
+    torch.cuda.synchronize()
+    for what, (a, e, s) in {"fwd": (lp, ent, lse), "fwd_bwd": (flp, fent, flse),
+                            "chunked": (clp, cent, clse)}.items():
+        assert_close(host(a), olp, tl, f"{what} logprob")
+        assert_close(host(e), oent, te, f"{what} entropy")
+        assert_close(host(s), olse, tl, f"{what} lse")
+        assert np.all(host(a)[ign] == 0) and not np.any(np.signbit(host(a)[ign])), what
+    for what, x in {"bwd": g, "fwd_bwd": fg}.items():
+        gx = host(x)
+        assert_close(gx, og, tg, f"{what} grad")
+        assert np.all(gx[ign] == 0) and not np.any(np.signbit(gx[ign])), what
+    omlp, _, _ = orc.forward_multi(z, host(mlab), ignore_index=ii)
+    assert_close(host(mlp), omlp, tl, "multi logprob")
+    assert np.all(host(mlp)[:, 1] == 0) and not np.any(np.signbit(host(mlp)[:, 1]))
