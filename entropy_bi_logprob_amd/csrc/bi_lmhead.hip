@@ -123,13 +123,20 @@ struct LmArgs {
   const float* token_weights;   // [n_tok] or NULL (= 1)
   uint16_t* gout;           // [n_voc, ldg] bf16 bits: gradient of the logits, vocabulary-major
   int64_t ldg;
-  void* dout;               // [n_voc, ldd] fp32 or bf16: the product itself (product kernel)
+  void* dout;               // [n_voc, ldd] fp32 or bf16: the product itself (product kernels)
   int64_t ldd;
   int dout_bf16;
+  int64_t gpad;             // grad-logits kernel: rows n_voc .. gpad-1 of gout written as zeros
+  int64_t kvalid_h;         // transposed product: rows of the H-side operand that exist
 };
 
-// What a workgroup does with its fp32 tile of D = W . H^T
-enum { kModeStats = 0, kModeGrad = 1, kModeProduct = 2 };
+// What a workgroup does with its fp32 tile of D = W . H^T:
+//   kModeStats     per-token statistics of each 256-row vocabulary tile;
+//   kModeGrad      the gradient of the logits, bf16, vocabulary-major;
+//   kModeProduct   D itself, fp32 or bf16, operands with K contiguous;
+//   kModeProductT  D added into an fp32 output, operands with M (N) contiguous:
+//                  "W" is stored [K][n_voc] and "H" [K][n_tok].
+enum { kModeStats = 0, kModeGrad = 1, kModeProduct = 2, kModeProductT = 3 };
 
 // Tile (tv, tn) of linear tile index t: groups of kGroup token tiles sweep
 // the vocabulary tiles together.
@@ -185,13 +192,15 @@ typedef __attribute__((address_space(3))) void lds_void;
 // clamped to the tile's last valid row, at the chunk that its LDS position
 // holds; the tile bases are uniform (SGPRs) and the lane's offset is 32-bit.
 struct LmFill {
-  const char* wbase;   // W row v0
-  const char* hbase;   // H row n0
+  const char* wbase;   // W row v0 (transposed: K-row 0, column v0)
+  const char* hbase;   // H row n0 (transposed: K-row 0, column n0)
   uint32_t ldw2, ldh2; // row pitches in bytes
   int wlast, hlast;    // last valid operand row within the tile
-  int row0;            // this lane's first row
+  int row0;            // this lane's first row (transposed: its first K-row of a stage)
   uint32_t cbytes;     // byte offset of the chunk this lane's slot holds
   uint32_t lds0;       // this wave's first block: wave * 1 KB
+  uint32_t wc, hc;     // transposed: the lane's chunk offset, clamped per side
+  int64_t wklast, hklast;   // transposed: last K-row that exists, per side
 };
 
 // A pointer that is the same in every lane, marked so for the compiler (the
@@ -203,9 +212,36 @@ __device__ inline const char* uniform_ptr(const char* q) {
   return reinterpret_cast<const char*>((uint64_t(hi) << 32) | lo);
 }
 
+// Transposed operands (kModeProductT) are stored [K][columns]: a unit holds
+// the stage's 64 K-rows of the tile's 256 columns, 512 bytes each, and the
+// 16-byte chunk c of K-row k sits in chunk c ^ lm_swz_t(k).  A wave's request
+// covers two K-rows (1 KB); request i of a lane reads K-row
+// row0 + 2 kWaves i of the stage, clamped to the last K-row that exists, at
+// the chunk its LDS position holds, clamped to the last chunk with columns in
+// the tile (so nothing is read past a row's end; the columns past the tile's
+// end are never stored).
+constexpr int kTRowBytes = kTV * 2;
+static_assert(kBK * kTRowBytes == kUnitBytes, "transposed unit = one stage's K-rows");
+__device__ inline int lm_swz_t(int k) { return 4 * (k & 3); }
+
+template <int MODE>
 __device__ inline LmFill lm_fill_setup(const LmArgs& p, int64_t v0, int64_t n0, int wave,
                                        int lane) {
   LmFill f;
+  if constexpr (MODE == kModeProductT) {
+    f.row0 = 2 * wave + (lane >> 5);
+    const int lc = (lane & 31) ^ lm_swz_t(f.row0);   // lm_swz_t(row0 + 2 kWaves i) == lm_swz_t(row0)
+    f.wc = uint32_t(16 * min(lc, int((min(p.n_voc - v0, int64_t(kTV)) - 1) >> 3)));
+    f.hc = uint32_t(16 * min(lc, int((min(p.n_tok - n0, int64_t(kTN)) - 1) >> 3)));
+    f.wbase = uniform_ptr(reinterpret_cast<const char*>(p.weight + v0));
+    f.hbase = uniform_ptr(reinterpret_cast<const char*>(p.hidden + n0));
+    f.ldw2 = uint32_t(p.ldw * 2);
+    f.ldh2 = uint32_t(p.ldh * 2);
+    f.wklast = p.d - 1;
+    f.hklast = p.kvalid_h - 1;
+    f.lds0 = uint32_t(wave) * 1024u;
+    return f;
+  }
   const int rb = lane / kChunks, slot = lane % kChunks;
   f.row0 = kBlockRows * wave + rb;
   f.cbytes = uint32_t(16 * (slot ^ lm_swz(f.row0)));   // lm_swz(row0 + 64 i) == lm_swz(row0)
@@ -237,22 +273,36 @@ __device__ inline uint32_t lds_addr(const char* p) {
 // them stricter.  The LDS-DMA load reads M0, which the compiler writes just
 // before the asm with a scalar instruction: one wait state (s_nop 0) must
 // separate the two.
+// (Transposed: the stage's K-row 0 is the uniform base, so the offset is at
+// most 63 pitches plus 512 bytes.)
+template <int MODE>
 __device__ inline void lm_fill1(const LmFill& f, uint32_t slot, int stage, bool is_w, int i) {
-  const int row = min(f.row0 + kBlockRows * kWaves * i, is_w ? f.wlast : f.hlast);
-  const uint32_t off = uint32_t(row) * (is_w ? f.ldw2 : f.ldh2) + f.cbytes +
-                       uint32_t(stage) * kRowBytes;
+  const char* base;
+  uint32_t off;
+  if constexpr (MODE == kModeProductT) {
+    const int64_t k0 = int64_t(stage) * kBK;
+    const uint32_t pitch = is_w ? f.ldw2 : f.ldh2;
+    const int lim = int(min((is_w ? f.wklast : f.hklast) - k0, int64_t(kBK - 1)));
+    const int kr = min(f.row0 + 2 * kWaves * i, lim);
+    base = uniform_ptr((is_w ? f.wbase : f.hbase) + k0 * pitch);
+    off = uint32_t(kr) * pitch + (is_w ? f.wc : f.hc);
+  } else {
+    const int row = min(f.row0 + kBlockRows * kWaves * i, is_w ? f.wlast : f.hlast);
+    base = is_w ? f.wbase : f.hbase;
+    off = uint32_t(row) * (is_w ? f.ldw2 : f.ldh2) + f.cbytes + uint32_t(stage) * kRowBytes;
+  }
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                :
-               : "v"(off), "s"(is_w ? f.wbase : f.hbase),
-                 "{m0}"(slot + f.lds0 + uint32_t(kWaves * i) * 1024u)
+               : "v"(off), "s"(base), "{m0}"(slot + f.lds0 + uint32_t(kWaves * i) * 1024u)
                : "memory");
 }
 
 // Request i of unit u (0 <= i < kLoadsU) into the ring at LDS address `ring`;
 // units past the last stage (u >= 2 ns) are not requested.
+template <int MODE>
 __device__ inline void lm_fill_unit1(const LmFill& f, uint32_t ring, int u, int ns, int i) {
   if ((u >> 1) < ns)
-    lm_fill1(f, ring + uint32_t(u % kSlots) * kUnitBytes, u >> 1, (u & 1) == 0, i);
+    lm_fill1<MODE>(f, ring + uint32_t(u % kSlots) * kUnitBytes, u >> 1, (u & 1) == 0, i);
 }
 
 // Wait until at most n of this wave's newest units are still in flight
@@ -271,23 +321,85 @@ struct LmFrag {
   bf16x8 a[kXB], b[kYB];
 };
 
-// Operand fragment j of one K step of the stage whose W and H units are in
+// The lane's fragment offsets within a unit.  K-major operands: the 16 bytes
+// of each K step (row lr of the wave's first block, chunk 2 kk + half).
+// Transposed operands: for block x (y), the 8 bytes this lane supplies to a
+// transposing read of K-rows 0..3 of the step (the reads of K-rows 4..7 and of
+// later steps are fixed distances on).
+struct LmOffs {
+  uint32_t w[kKS], h[kKS];
+  uint32_t tw[kXB], th[kYB];
+};
+
+template <int MODE>
+__device__ inline LmOffs lm_offsets(int wv, int wt, int lane) {
+  LmOffs o;
+  const int lr = lane & 31, half = lane >> 5;
+  if constexpr (MODE == kModeProductT) {
+    // ds_read_b64_tr_b16: within each 16-lane group, lane i receives the
+    // 16-bit element i % 4 of the 8 bytes that lanes i / 4, 4 + i / 4,
+    // 8 + i / 4 and 12 + i / 4 supply.  Lane 4e + q of group g supplies K-row
+    // e (+8 for groups 2 and 3) at columns 4q .. 4q+3 (+16 for groups 1 and
+    // 3) of the block, so lane l receives column l % 32 at K 8 (l / 32) + 0..3:
+    // the MFMA operand's layout.  The K-row's swizzle is lm_swz_t(e).
+    const int g = lane >> 4, e = (lane >> 2) & 3, q = lane & 3;
+    const uint32_t lane_off = uint32_t((8 * (g >> 1) + e) * kTRowBytes + 8 * (q & 1));
+    const int cl = 2 * (g & 1) + (q >> 1);   // chunk within the block's four
+#pragma unroll
+    for (int x = 0; x < kXB; ++x)
+      o.tw[x] = lane_off + uint32_t(16 * ((((kWV * wv + 32 * x) >> 3) ^ lm_swz_t(e)) + cl));
+#pragma unroll
+    for (int y = 0; y < kYB; ++y)
+      o.th[y] = lane_off + uint32_t(16 * ((((kWN * wt + 32 * y) >> 3) ^ lm_swz_t(e)) + cl));
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < kKS; ++kk) {
+      const uint32_t in_row = uint32_t(lr * kRowBytes + 16 * ((2 * kk + half) ^ lm_swz(lr)));
+      o.w[kk] = uint32_t(kWV * wv * kRowBytes) + in_row;
+      o.h[kk] = uint32_t(kWN * wt * kRowBytes) + in_row;
+    }
+  }
+  return o;
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// K-rows 0..7 of a transposed fragment: two transposing reads 4 K-rows apart
+__device__ inline bf16x8 lm_read_t(const char* p) {
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * kTRowBytes));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Operand fragment j of K step kk of the stage whose W and H units are in
 // the slots w and h, in the order the step's MFMAs first use them (A0,
 // B0 .. B(kYB-1), A1 ..).
-__device__ inline void lm_read1(LmFrag& fr, const char* w, const char* h, uint32_t off_w,
-                                uint32_t off_h, int j) {
-  if (j >= 1 && j <= kYB) {
-    fr.b[j - 1] = *reinterpret_cast<const bf16x8*>(h + off_h + (j - 1) * 32 * kRowBytes);
+template <int MODE>
+__device__ inline void lm_read1(LmFrag& fr, const char* w, const char* h, const LmOffs& o,
+                                int kk, int j) {
+  if constexpr (MODE == kModeProductT) {
+    const int kbytes = 16 * kk * kTRowBytes;
+    if (j >= 1 && j <= kYB) {
+      fr.b[j - 1] = lm_read_t(h + o.th[j - 1] + kbytes);
+    } else {
+      const int x = j == 0 ? 0 : j - kYB;
+      fr.a[x] = lm_read_t(w + o.tw[x] + kbytes);
+    }
+  } else if (j >= 1 && j <= kYB) {
+    fr.b[j - 1] = *reinterpret_cast<const bf16x8*>(h + o.h[kk] + (j - 1) * 32 * kRowBytes);
   } else {
     const int x = j == 0 ? 0 : j - kYB;
-    fr.a[x] = *reinterpret_cast<const bf16x8*>(w + off_w + x * 32 * kRowBytes);
+    fr.a[x] = *reinterpret_cast<const bf16x8*>(w + o.w[kk] + x * 32 * kRowBytes);
   }
 }
 
-__device__ inline void lm_read(LmFrag& fr, const char* w, const char* h, uint32_t off_w,
-                               uint32_t off_h) {
+template <int MODE>
+__device__ inline void lm_read(LmFrag& fr, const char* w, const char* h, const LmOffs& o,
+                               int kk) {
 #pragma unroll
-  for (int j = 0; j < kXB + kYB; ++j) lm_read1(fr, w, h, off_w, off_h, j);
+  for (int j = 0; j < kXB + kYB; ++j) lm_read1<MODE>(fr, w, h, o, kk, j);
 }
 
 constexpr int kMfmas = kXB * kYB;                      // MFMAs per wave per K step
@@ -440,7 +552,11 @@ __device__ inline uint32_t pack_bf16(float lo, float hi) {
 // kModeProduct: the product itself, fp32 or bf16 (RNE), for the lm_head
 //               backward's G^T . hidden with the operands' roles taken by G
 //               and the transposed hidden states.
-// Same main loop, same product bits, in every mode.
+// kModeProductT: the product of two operands stored [K][columns], added into
+//               an fp32 output: the lm_head backward's grad_hidden += G . W_c
+//               with G vocabulary-major and the lm_head rows as they are.
+// Same main loop, same product bits, in the first three modes; the fourth
+// reads its fragments with transposing LDS reads.
 template <int MODE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEU, kWavesPerEU)))
 void lmhead_kernel(LmArgs p) {
@@ -461,24 +577,18 @@ void lmhead_kernel(LmArgs p) {
   for (int y = 0; y < kYB; ++y) {
     const int64_t j = n0 + kWN * wt + 32 * y + lr;
     const bool in = j < p.n_tok;
-    if constexpr (MODE != kModeProduct) lab[y] = in ? p.labels[j] : p.ignore_index;
+    if constexpr (MODE == kModeStats || MODE == kModeGrad)
+      lab[y] = in ? p.labels[j] : p.ignore_index;
     if constexpr (MODE == kModeGrad) {
       tlse[y] = in ? p.lse[j] : 0.0f;
       tw[y] = in && p.token_weights ? p.token_weights[j] : 1.0f;
     }
   }
 
-  const LmFill fill = lm_fill_setup(p, v0, n0, wave, lane);
+  const LmFill fill = lm_fill_setup<MODE>(p, v0, n0, wave, lane);
   const int ns = int(p.d / kBK);
 
-  // this lane's fragment offsets within a stage, for each K step
-  uint32_t off_w[kKS], off_h[kKS];
-#pragma unroll
-  for (int kk = 0; kk < kKS; ++kk) {
-    const uint32_t in_row = uint32_t(lr * kRowBytes + 16 * ((2 * kk + half) ^ lm_swz(lr)));
-    off_w[kk] = uint32_t(kWV * wv * kRowBytes) + in_row;
-    off_h[kk] = uint32_t(kWN * wt * kRowBytes) + in_row;
-  }
+  const LmOffs offs = lm_offsets<MODE>(wv, wt, lane);
 
   f32x16 acc[kXB][kYB];
 #pragma unroll
@@ -502,11 +612,11 @@ void lmhead_kernel(LmArgs p) {
 #pragma unroll
   for (int u = 0; u < kPrologue; ++u)
 #pragma unroll
-    for (int i = 0; i < kLoadsU; ++i) lm_fill_unit1(fill, rbase, u, ns, i);
+    for (int i = 0; i < kLoadsU; ++i) lm_fill_unit1<MODE>(fill, rbase, u, ns, i);
   wait_units(min(kPrologue, 2 * ns) - 2);   // units 2 .. min(kPrologue, 2 ns) - 1 may fly on
   lds_barrier();
   LmFrag fr[2];
-  lm_read(fr[0], ring, ring + kUnitBytes, off_w[0], off_h[0]);
+  lm_read<MODE>(fr[0], ring, ring + kUnitBytes, offs, 0);
 
   // Stage s from the slots of units 2s (W) and 2s+1 (H), K step kk's
   // fragments in fr[kk & 1]: the next step's fragments are read while this
@@ -537,14 +647,14 @@ void lmhead_kernel(LmArgs p) {
       LmFrag& next = fr[(kk + 1) & 1];
       if (kk + 1 < kKS) {
         lm_mma_with(now, acc, [&](int m) {
-          if (m < kXB + kYB) lm_read1(next, wbuf, hbuf, off_w[kk + 1], off_h[kk + 1], m);
+          if (m < kXB + kYB) lm_read1<MODE>(next, wbuf, hbuf, offs, kk + 1, m);
           if constexpr (kSpread) {
             // request r goes out in step r (kKS-1) / kLoadsU, after the step's reads
 #pragma unroll
             for (int r = 0; r < kLoadsU; ++r)
               if (r * (kKS - 1) / kLoadsU == kk &&
                   m == kXB + kYB + r - (kk * kLoadsU + kKS - 2) / (kKS - 1) && pending)
-                lm_fill1(fill, fp, s + 2, true, r);
+                lm_fill1<MODE>(fill, fp, s + 2, true, r);
           }
         });
       } else {
@@ -563,19 +673,19 @@ void lmhead_kernel(LmArgs p) {
             // only unit 2s+5 (H of stage s+2) now, every other MFMA; unit
             // 2s+6 is the next stage's spread W unit
             if (m % 2 == 0 && m / 2 < kLoadsU && (!TAIL || sa < ns))
-              lm_fill1(fill, fa, sa, false, m / 2);
+              lm_fill1<MODE>(fill, fa, sa, false, m / 2);
           } else {
 #pragma unroll
             for (int q = 0; q < kFillsPerMfma; ++q) {
               const int r = m * kFillsPerMfma + q;
               if (r < kLoadsU) {
-                if (!TAIL || sa < ns) lm_fill1(fill, fa, sa, kSlots % 2 == 0, r);
+                if (!TAIL || sa < ns) lm_fill1<MODE>(fill, fa, sa, kSlots % 2 == 0, r);
               } else if (r < kLoads) {
-                if (!TAIL || sb < ns) lm_fill1(fill, fb, sb, kSlots % 2 == 1, r - kLoadsU);
+                if (!TAIL || sb < ns) lm_fill1<MODE>(fill, fb, sb, kSlots % 2 == 1, r - kLoadsU);
               }
             }
           }
-          if (m < kXB + kYB) lm_read1(next, nwbuf, nhbuf, off_w[0], off_h[0], m);
+          if (m < kXB + kYB) lm_read1<MODE>(next, nwbuf, nhbuf, offs, 0, m);
         });
       }
     }
@@ -587,7 +697,24 @@ void lmhead_kernel(LmArgs p) {
   wait_counts<0, 15>();   // no request may still be writing LDS when the workgroup ends
   lds_barrier();          // every wave is done with the ring: the epilogues reuse it
 
-  if constexpr (MODE == kModeProduct) {
+  if constexpr (MODE == kModeProductT) {
+    // D[i][j] += the tile, fp32, for the rows and columns that exist (the
+    // W side's columns are D's rows); for a given accumulator register the 64
+    // lanes cover 32 consecutive columns of 2 rows
+    float* dout = static_cast<float*>(p.dout);
+#pragma unroll
+    for (int x = 0; x < kXB; ++x)
+#pragma unroll
+      for (int y = 0; y < kYB; ++y) {
+        const int64_t j = n0 + kWN * wt + 32 * y + lr;
+        if (j >= p.n_tok) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t i = v0 + kWV * wv + 32 * x + 8 * (r >> 2) + 4 * half + (r & 3);
+          if (i < p.n_voc) dout[i * p.ldd + j] += acc[x][y][r];
+        }
+      }
+  } else if constexpr (MODE == kModeProduct) {
     // D[i][j] for the rows and columns that exist; for a given accumulator
     // register the 64 lanes cover 32 consecutive columns of 2 rows
 #pragma unroll
@@ -677,15 +804,18 @@ void lmhead_kernel(LmArgs p) {
     }
     wait_counts<63, 0>();
     lds_barrier();
-    // rows v0 .. v0+255, 16-byte chunks of 8 tokens; 32 threads per row
+    // rows v0 .. v0+255, 16-byte chunks of 8 tokens; 32 threads per row.
+    // Rows n_voc .. gpad-1 (the lm_head backward pads its chunk to whole K
+    // stages) are written as zeros.
     const bool vec = (p.ldg % 8) == 0 && (reinterpret_cast<uintptr_t>(p.gout) % 16) == 0;
     constexpr int kChunksPerRow = kTN / 8;
 #pragma unroll 4
     for (int q = tid; q < kTV * kChunksPerRow; q += kThreads) {
       const int row = q / kChunksPerRow, c = q % kChunksPerRow;
       const int64_t i = v0 + row, j0 = n0 + 8 * c;
-      if (i >= p.n_voc || j0 >= p.n_tok) continue;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(ring + lm_grad_at(row, 8 * c));
+      if (i >= p.gpad || j0 >= p.n_tok) continue;
+      u32x4 v = *reinterpret_cast<const u32x4*>(ring + lm_grad_at(row, 8 * c));
+      if (i >= p.n_voc) v = u32x4{0u, 0u, 0u, 0u};
       uint16_t* dst = p.gout + i * p.ldg + j0;
       if (vec && j0 + 8 <= p.n_tok) {
         *reinterpret_cast<u32x4*>(dst) = v;
@@ -816,7 +946,25 @@ int bi_lmhead_grad_logits(const void* hidden, const void* weight, int64_t n_toke
                           const int64_t* labels, int64_t ignore_index, const float* lse,
                           const float* token_weights, void* grad_logits, int64_t grad_stride,
                           int32_t* status_flag, bi_stream_t stream) {
-  const char* fn = "bi_lmhead_grad_logits";
+  return lmhead_grad_logits_padded("bi_lmhead_grad_logits", hidden, weight, n_tokens,
+                                   n_vocab_rows, d, hidden_stride, weight_stride, vocab_offset,
+                                   vocab, labels, ignore_index, lse, token_weights, grad_logits,
+                                   grad_stride, n_vocab_rows, status_flag, stream);
+}
+
+}  // extern "C"
+
+namespace bi_internal {
+
+int lmhead_grad_logits_padded(const char* fn, const void* hidden, const void* weight,
+                              int64_t n_tokens, int64_t n_vocab_rows, int64_t d,
+                              int64_t hidden_stride, int64_t weight_stride, int64_t vocab_offset,
+                              int64_t vocab, const int64_t* labels, int64_t ignore_index,
+                              const float* lse, const float* token_weights, void* grad_logits,
+                              int64_t grad_stride, int64_t pad_rows, int32_t* status_flag,
+                              bi_stream_t stream) {
+  if (pad_rows < n_vocab_rows || pad_rows > (n_vocab_rows + kTV - 1) / kTV * kTV)
+    return fail(BI_ERR_SHAPE, "%s: padded rows outside the last tile", fn);
   LmArgs a{};
   if (int r = lm_setup(fn, &a, hidden, weight, n_tokens, n_vocab_rows, d, hidden_stride,
                        weight_stride, vocab_offset, vocab, labels, ignore_index, status_flag))
@@ -832,7 +980,38 @@ int bi_lmhead_grad_logits(const void* hidden, const void* weight, int64_t n_toke
   a.token_weights = token_weights;
   a.gout = static_cast<uint16_t*>(grad_logits);
   a.ldg = grad_stride;
+  a.gpad = pad_rows;
   return lm_launch<kModeGrad>(fn, a, stream);
 }
 
-}  // extern "C"
+// D[i][j] += sum_k A[k][i] B[k][j]: A [k][m] and B [k][n] bf16 with rows of
+// m (n) contiguous elements, of which B has only its first kvalid_b rows
+// (the rest read as row kvalid_b - 1; A's rows there must be zero); D fp32.
+int lmhead_product_t(const char* fn, const void* a, int64_t m, int64_t lda, const void* b,
+                     int64_t n, int64_t ldb, int64_t k, int64_t kvalid_b, float* d, int64_t ldd,
+                     bi_stream_t stream) {
+  if (k < kBK || k % kBK != 0 || k > (int64_t(1) << 31) - kBK || kvalid_b < 1 ||
+      kvalid_b > k || kvalid_b <= k - kBK || lda < m || ldb < n || lda % 8 || ldb % 8 ||
+      lda > (int64_t(1) << 22) || ldb > (int64_t(1) << 22) || ldd < n || m > 0x7fffffff ||
+      n > 0x7fffffff)
+    return fail(BI_ERR_SHAPE, "%s: transposed product shape outside the kernel's limits", fn);
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(d, 4))
+    return fail(BI_ERR_ALIGN, "%s: misaligned product operand", fn);
+  if (m == 0 || n == 0) return BI_OK;
+  LmArgs p{};
+  p.weight = static_cast<const uint16_t*>(a);
+  p.hidden = static_cast<const uint16_t*>(b);
+  p.n_voc = m;
+  p.n_tok = n;
+  p.d = k;
+  p.ldw = lda;
+  p.ldh = ldb;
+  p.kvalid_h = kvalid_b;
+  p.dout = d;
+  p.ldd = ldd;
+  p.tiles_v = (m + kTV - 1) / kTV;
+  p.tiles_n = (n + kTN - 1) / kTN;
+  return lm_launch<kModeProductT>(fn, p, stream);
+}
+
+}  // namespace bi_internal

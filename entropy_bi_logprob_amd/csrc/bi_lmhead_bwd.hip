@@ -11,21 +11,23 @@
 // "ZeroSyncGRPOTrainer" (bf16 GEMMs with fp32 accumulation).
 //
 // How: the vocabulary shard is cut into chunks of rows that fit the caller's
-// workspace.  For each chunk, bi_lmhead_grad_logits recomputes its logits on
+// workspace.  For each chunk, the grad-logits kernel recomputes its logits on
 // the matrix cores (the forward's exact MFMA sequence) and writes G for the
-// chunk as bf16, vocabulary-major [rows][n_tokens]; then G @ W_chunk is added
-// into grad_hidden by a plain library GEMM (hipBLASLt, bf16 operands, fp32
-// accumulation), and G^T @ hidden is written into the chunk's grad_weight
-// rows.  That second product has G's rows, token-contiguous, as one operand:
-// when n_tokens is a multiple of 64 (at most 2^22) and the workspace holds a
-// transposed copy of the hidden states ([d][n_tokens], made once per call),
-// it runs on the lm_head kernel's own matrix-core pipeline, otherwise on
-// hipBLASLt too.  All of it is queued on the caller's stream; hipBLASLt
-// works in the first part of the caller's workspace, so nothing here
-// allocates device memory except the per-device hipBLASLt handle, created on
-// the first call on a device.  The algorithm of each library GEMM shape is
-// chosen once by hipBLASLt's heuristic and kept, so a shape always runs the
-// same kernel (reproducible results).
+// chunk as bf16, vocabulary-major [rows][n_tokens], its rows padded with
+// zeros to a multiple of 64; then G @ W_chunk is added into grad_hidden and
+// G^T @ hidden written into the chunk's grad_weight rows (bf16 operands, fp32
+// accumulation).  G @ W_chunk has both operands stored [K][columns] (G by
+// vocabulary row, W_chunk as the lm_head rows are): it runs on the lm_head
+// kernel's pipeline with transposing LDS reads.  G^T @ hidden has G's rows,
+// token-contiguous, as one operand: when n_tokens is a multiple of 64 (at
+// most 2^22) and the workspace holds a transposed copy of the hidden states
+// ([d][n_tokens], made once per call), it runs on the same pipeline.  Outside
+// those limits a product runs on hipBLASLt (a plain library GEMM), which
+// works in the first part of the caller's workspace.  All of it is queued on
+// the caller's stream; nothing here allocates device memory except the
+// per-device hipBLASLt handle, created on the first call that needs it.  The
+// algorithm of each library GEMM shape is chosen once by hipBLASLt's
+// heuristic and kept, so a shape always runs the same kernel.
 
 #include <hip/hip_runtime.h>
 #include <hipblaslt/hipblaslt.h>
@@ -245,11 +247,18 @@ int bi_lmhead_backward(const void* hidden, const void* weight, int64_t n_tokens,
   uint16_t* ht = reinterpret_cast<uint16_t*>(ws + kBlasWorkspace);
   uint16_t* g = reinterpret_cast<uint16_t*>(ws + kBlasWorkspace + ht_bytes);
   const size_t gw_elem = grad_weight_dtype == BI_BF16 ? 2 : 4;
+  // grad_hidden += G . W_c on the matrix-core pipeline with transposing reads
+  // (G vocabulary-major and W_c as stored are both [K][columns]) while G's
+  // row pitch is within its limit; else on the library
+  const bool own_dh = ldg <= (int64_t(1) << 22);
 
-  std::lock_guard<std::mutex> lock(g_blas_mutex);
+  std::unique_lock<std::mutex> lock(g_blas_mutex, std::defer_lock);
   int dev = -1;
   hipblasLtHandle_t h = nullptr;
-  if (int r = lt_handle(fn, &dev, &h)) return r;
+  if (!own || !own_dh) {   // the library is needed: its handle, made once per device
+    lock.lock();
+    if (int r = lt_handle(fn, &dev, &h)) return r;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const hipDataType gw_type = grad_weight_dtype == BI_BF16 ? HIP_R_16BF : HIP_R_32F;
   if (own) {
@@ -262,18 +271,28 @@ int bi_lmhead_backward(const void* hidden, const void* weight, int64_t n_tokens,
   }
   for (int64_t c0 = 0; c0 < n_vocab_rows; c0 += chunk) {
     const int64_t rows = n_vocab_rows - c0 < chunk ? n_vocab_rows - c0 : chunk;
+    // G's rows up to the next multiple of 64 (within the chunk buffer, whose
+    // row count is a multiple of 256 or covers the whole shard's last tile)
+    const int64_t kpad = (rows + 63) / 64 * 64;
     const uint16_t* wc = static_cast<const uint16_t*>(weight) + c0 * weight_stride;
-    if (int r = bi_lmhead_grad_logits(hidden, wc, n_tokens, rows, d, hidden_stride,
-                                      weight_stride, vocab_offset + c0, vocab, labels,
-                                      ignore_index, lse, token_weights, g, ldg, status_flag,
-                                      stream))
+    if (int r = lmhead_grad_logits_padded(fn, hidden, wc, n_tokens, rows, d, hidden_stride,
+                                          weight_stride, vocab_offset + c0, vocab, labels,
+                                          ignore_index, lse, token_weights, g, ldg,
+                                          own_dh ? kpad : rows, status_flag, stream))
       return r;
-    // column-major view: grad_hidden^T (d x N) += W_c^T (d x rows) . (G^T: rows x N)
-    const Gemm dh{HIPBLAS_OP_N, HIPBLAS_OP_T, d, n_tokens, rows, weight_stride, ldg,
-                  grad_hidden_stride, HIP_R_32F};
-    if (int r = lt_gemm(fn, h, dev, dh, wc, g, 1.0f, grad_hidden, workspace,
-                        size_t(kBlasWorkspace), s))
-      return r;
+    if (own_dh) {
+      // grad_hidden[n][c] += sum_v G[v][n] W_c[v][c]; G's padding rows are zero
+      if (int r = lmhead_product_t(fn, g, n_tokens, ldg, wc, d, weight_stride, kpad, rows,
+                                   grad_hidden, grad_hidden_stride, stream))
+        return r;
+    } else {
+      // column-major view: grad_hidden^T (d x N) += W_c^T (d x rows) . (G^T: rows x N)
+      const Gemm dh{HIPBLAS_OP_N, HIPBLAS_OP_T, d, n_tokens, rows, weight_stride, ldg,
+                    grad_hidden_stride, HIP_R_32F};
+      if (int r = lt_gemm(fn, h, dev, dh, wc, g, 1.0f, grad_hidden, workspace,
+                          size_t(kBlasWorkspace), s))
+        return r;
+    }
     void* gwc = static_cast<char*>(grad_weight) + c0 * grad_weight_stride * int64_t(gw_elem);
     if (own) {
       // grad_weight_c[v][c] = sum_n G[v][n] ht[c][n]
