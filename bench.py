@@ -38,7 +38,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=32768)
     ap.add_argument("--profile-steps", type=int, default=None,
-                    help="run only this many steps (for profilers); still prints the line")
+                    help="run only this many steps, after one warm-up step (for profilers); "
+                         "still prints the line")
     ap.add_argument("--no-lmhead", action="store_true",
                     help="skip the lm_head-projection leg (GEMM + statistics on matrix cores)")
     ap.add_argument("--calibrate-copy-gib", type=float, default=0.0,
@@ -173,7 +174,9 @@ def lmhead_leg(bi, torch, np, wl, N, V, seed, steps, warm, stream, with_cpu=True
                 "ms": t_bwd, "TFLOPs_3gemm": tfb,
                 "roofline": {"bound": "mfma", "achieved": tfb, "peak": MFMA_BF16_PEAK_TFLOPS,
                              "unit": "TFLOP/s", "frac": tfb / MFMA_BF16_PEAK_TFLOPS,
-                             "traffic": None},
+                             "traffic": (measured_traffic("lmhead_backward", LMHEAD_SUMMARY,
+                                                          LMHEAD_SOURCES)
+                                         if (N, V, d) == (32768, 151936, 2560) else None)},
                 "unfused_ms": sum(t_ub), "unfused_parts_ms": t_ub,
                 "unfused_what": "torch.matmul logits, bi_logprob_bwd to bf16, two torch.matmul "
                                 "(20 GB of logits and gradient)",
@@ -321,7 +324,9 @@ def main():
         del src, dst
 
     steps = args.profile_steps or args.steps
-    warm = 0 if args.profile_steps else args.warmup
+    # a profiled run still takes one warm-up step, so the traced averages are
+    # not skewed by a first call on cold caches and clocks
+    warm = min(args.warmup, 1) if args.profile_steps else args.warmup
     for _ in range(warm):
         step_fused()
         step_two_calls()
