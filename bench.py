@@ -354,6 +354,17 @@ def main():
     ms_policy, (t_policy,) = timed(step_policy, 2)
     assert int(flag.item()) == 0
 
+    # same-run reference for the fused kernel's HBM traffic: a library copy of
+    # the logits into the gradient buffer reads and writes exactly the bytes the
+    # fused kernel must move (its re-read comes from the caches)
+    def step_copy(ev=None):
+        if ev: ev[0].record(stream)
+        torch.neg(logits, out=grad)
+        if ev: ev[1].record(stream)
+
+    step_copy()
+    _, (t_copy,) = timed(step_copy, 2)
+
     f_b, b_b, c_b, m_b = algorithmic_bytes(V, 2, 2, len(bounds))
     fused_b = V * (2 + 2) + 8 + 4 + 12       # one read of the logits, one write of the grad
     med = lambda xs: float(np.median(xs))
@@ -410,6 +421,11 @@ def main():
                      "kernel": "fused fwd+bwd (bf16 logits, bf16 grad)",
                      "bytes_per_launch": kernels[dom]["bytes"]},
         "kernels": kernels,
+        "reference_copy": {
+            "what": "torch.neg(logits, out=grad): a library copy of the same tensor, one read "
+                    "and one write per element (the fused kernel's HBM bytes), same run",
+            "ms": mean(t_copy), "GBps": gbps(2 * N * V * 2, mean(t_copy)),
+            "fused_kernel_vs_copy": mean(t_copy) / mean(t_fused)},
         "two_call": two_call,
         "chunked": chunked,
         "policy_loss": policy,

@@ -228,6 +228,53 @@ def test_bwd_writes_every_element_deterministically(V, dt, gdt):
     assert torch.equal(g1.view(ity), g2.view(ity))
 
 
+@pytest.mark.parametrize("dt,gdt,V", [("bf16", torch.bfloat16, 151_936),
+                                      ("bf16", torch.float32, 131_072),
+                                      ("bf16", torch.bfloat16, 151_938),
+                                      ("f32", torch.float32, 65_539),
+                                      ("f32", torch.float32, 30_000)])
+def test_bwd_sweep_equals_row_kernel(dt, gdt, V):
+    # wide rows on 4-byte boundaries take the backward as a sweep of 256-vector
+    # pieces; the fused kernel's second pass and (for bf16) rows on 2-byte
+    # boundaries walk whole rows.  The gradients must agree bit for bit, with
+    # labels on both sides of every piece seam, in the first and last columns
+    # and in a ragged tail, ignored rows, one bad label, and a padded row pitch.
+    n, vec = 37, (8 if dt == "bf16" else 4)
+    seam = 256 * vec                         # elements per piece
+    b = random_batch(n, V, dt, seed=V + 11, ignore_frac=0.15, mask_frac=0.05)
+    labels = b.labels.copy()
+    for r in range(n):
+        if labels[r] != -100 and r % 3 != 2:
+            k = 1 + (r * 7) % (V // seam - 1)    # a seam inside the row
+            labels[r] = k * seam if r % 3 == 0 else k * seam - 1
+    labels[1], labels[2], labels[4], labels[5] = 0, V - 1, V - 1 - (V % vec) // 2, V + 3
+    logits, lab, w = dev_logits(b.logits, dt), dev(labels), dev(b.weights)
+    f1 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    lp, ent, lse = bi.fwd(logits, lab)
+    sweep = bi.bwd(logits, lab, lse, w, gdt, status=f1)
+    _, _, flse, fused = bi.fwd_bwd(logits, lab, w, gdt)
+    wide = torch.zeros((n, V + 64), dtype=logits.dtype, device="cuda")
+    wide[:, :V] = logits
+    gwide = torch.full((n, V + 8), float("nan"), dtype=gdt, device="cuda")
+    padded = bi.bwd(wide[:, :V], lab, lse, w, out=gwide[:, :V])
+    torch.cuda.synchronize()
+    assert int(f1.item()) != 0
+    ity = torch.int16 if gdt == torch.bfloat16 else torch.int32
+    assert torch.equal(lse.view(torch.int32), flse.view(torch.int32))
+    assert torch.equal(sweep.view(ity), fused.view(ity))
+    assert torch.equal(sweep.view(ity), padded.view(ity))
+    if dt == "bf16":
+        odd = torch.zeros(n * (V + 1) + 1, dtype=logits.dtype, device="cuda")
+        view = odd[1:].view(n, V + 1)[:, :V]          # rows on 2-byte boundaries
+        view.copy_(logits)
+        rowk = bi.bwd(view, lab, lse, w, gdt)
+        torch.cuda.synchronize()
+        assert torch.equal(sweep.view(ity), rowk.view(ity))
+    assert bool(torch.isnan(sweep[5].float()).all())
+    ign = torch.from_numpy(labels == -100).cuda()
+    assert int((sweep[ign].view(ity) != 0).sum().item()) == 0   # ignored rows: +0.0 everywhere
+
+
 def _fused_vs_two_calls(logits, labels, w, gdt):
     lp, ent, lse = bi.fwd(logits, labels)
     g = bi.bwd(logits, labels, lse, w, gdt)
