@@ -137,6 +137,8 @@ BI_API int bi_logprob_fwd(const void* logits, int dtype, int64_t n_rows, int64_t
  *   (dtype, grad_dtype) must be (F32, F32), (BF16, BF16) or (BF16, F32);
  *   a bf16 gradient is the fp32 value rounded to nearest even.
  *   grad_row_stride >= vocab.
+ * Elementwise given lse: each element's bits depend only on its logit and its
+ * row's lse, weight and label, however the rows are split over workgroups.
  */
 BI_API int bi_logprob_bwd(const void* logits, int dtype, int64_t n_rows, int64_t vocab,
                    int64_t row_stride, const int64_t* labels, int64_t ignore_index,
