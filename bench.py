@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--profile-steps", type=int, default=None,
                     help="run only this many steps, after one warm-up step (for profilers); "
                          "still prints the line")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workload shapes (256 x 151,936 fp32 forward, "
+                         "4,096 x 151,936 bf16 and 2,048 x 151,937 masked fp32 fwd + bwd)")
     ap.add_argument("--no-lmhead", action="store_true",
                     help="skip the lm_head-projection leg (GEMM + statistics on matrix cores)")
     ap.add_argument("--calibrate-copy-gib", type=float, default=0.0,
@@ -235,6 +238,92 @@ def cpu_baseline(rows_total, sample_rows, seed):
             "sample": f"{sample_rows} seeded rows of the 32768x151936 bf16 workload, "
                       f"fp64 numpy forward+backward, {threads} threads over 16-row blocks, "
                       f"{dt:.2f} s wall"}
+
+
+def configs_leg(bi, torch, np, wl, seed, steps, warm, stream, with_cpu=True):
+    """The pages' other workload shapes (256 x 151,936 fp32 forward; 4,096 x 151,936
+    bf16 and 2,048 x 151,937 masked fp32 forward + backward), all rows drawn as the
+    tests draw them, each timed on the GPU path, with the fp64 oracle timed on the
+    same rows beside it."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    dev = torch.device("cuda:0")
+    out = {}
+    for cfg in (1, 2, 3):
+        w = wl.WORKLOADS[cfg]
+        b = wl.draw(cfg, seed=seed)
+        bf16 = w.dtype == "bf16"
+        e_in = 2 if bf16 else 4
+        gdt = torch.bfloat16 if bf16 else torch.float32
+        e_g = 2 if bf16 else 4
+        host = b.logits.view(np.int16) if bf16 else b.logits
+        # a workload smaller than the 256 MB Infinity Cache is rotated over copies
+        # (1 GiB in all at least) so that every call reads its logits from HBM
+        size = w.rows * w.vocab * e_in
+        copies = max(1, -(-(1 << 30) // size))
+        logits = [torch.from_numpy(host).to(dev) for _ in range(copies)]
+        if bf16:
+            logits = [t.view(torch.bfloat16) for t in logits]
+        labels = torch.from_numpy(b.labels).to(dev)
+        weights = None if b.weights is None else torch.from_numpy(b.weights).to(dev)
+        outs = tuple(torch.empty(w.rows, dtype=torch.float32, device=dev) for _ in range(3))
+        grad = torch.empty((w.rows, w.vocab), dtype=gdt, device=dev) if w.backward else None
+        f_b, b_b, _, _ = algorithmic_bytes(w.vocab, e_in, e_g, 1)
+
+        def timed(fn):
+            for i in range(max(warm, 1)):
+                fn(logits[i % copies])
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(steps)]
+            for i, (e0, e1) in enumerate(ev):
+                e0.record(stream)
+                fn(logits[i % copies])
+                e1.record(stream)
+            torch.cuda.synchronize()
+            return float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+
+        def two_calls(z):
+            bi.fwd(z, labels, out=outs, stream=stream)
+            if grad is not None:
+                bi.bwd(z, labels, outs[2], weights, out=grad, stream=stream)
+
+        ms = timed(two_calls)
+        nbytes = w.rows * (f_b + (b_b if w.backward else 0))
+        res = {"rows": w.rows, "vocab": w.vocab, "logits_dtype": w.dtype,
+               "path": "bi_logprob_fwd + bi_logprob_bwd" if w.backward else "bi_logprob_fwd",
+               "ms": ms, "rows_per_s": w.rows / (ms * 1e-3),
+               "hbm_GBps": nbytes / (ms * 1e-3) / 1e9,
+               "pct_hbm_peak": 100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+               "logits_copies": copies}
+        if w.backward:
+            res["grad_dtype"] = "bf16" if bf16 else "f32"
+            fms = timed(lambda z: bi.fwd_bwd(z, labels, weights, out=outs, grad=grad,
+                                             stream=stream))
+            fb = w.rows * (w.vocab * (e_in + e_g) + 24)
+            res["fused"] = {"ms": fms, "rows_per_s": w.rows / (fms * 1e-3),
+                            "hbm_GBps": fb / (fms * 1e-3) / 1e9,
+                            "pct_hbm_peak": 100 * fb / (fms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+        if with_cpu:
+            import oracle.bi_oracle as orc
+
+            threads, block = wl.default_threads(), 16
+
+            def run(a):
+                z = orc.decode(b.logits[a:a + block], w.dtype)
+                lp, ent, lse = orc.forward(z, b.labels[a:a + block])
+                if w.backward:
+                    orc.backward(z, b.labels[a:a + block], lse,
+                                 None if b.weights is None else b.weights[a:a + block])
+
+            t0 = time.perf_counter()
+            with ThreadPoolExecutor(threads) as ex:
+                list(ex.map(run, range(0, w.rows, block)))
+            dt = time.perf_counter() - t0
+            res["cpu_oracle"] = {"rows_per_s": w.rows / dt, "cores": threads, "s": dt,
+                                 "sample": "all rows, fp64 numpy, 16-row blocks"}
+        out[w.name] = res
+        del logits, grad
+    return out
 
 
 def main():
@@ -434,6 +523,9 @@ def main():
     if not args.no_lmhead:
         line["lmhead"] = lmhead_leg(bi, torch, np, wl, N, V, seed, steps, warm, stream,
                                     with_cpu=not args.no_cpu_baseline and not args.profile_steps)
+    if not args.no_configs and not args.profile_steps:
+        line["configs"] = configs_leg(bi, torch, np, wl, seed, steps, warm, stream,
+                                      with_cpu=not args.no_cpu_baseline)
     if not args.no_cpu_baseline and not args.profile_steps:
         line["cpu_baseline"] = cpu_baseline(N, args.cpu_sample_rows, seed)
     print(json.dumps(line), flush=True)
