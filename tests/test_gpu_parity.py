@@ -232,7 +232,8 @@ def test_bwd_writes_every_element_deterministically(V, dt, gdt):
                                       ("bf16", torch.float32, 131_072),
                                       ("bf16", torch.bfloat16, 151_938),
                                       ("f32", torch.float32, 65_539),
-                                      ("f32", torch.float32, 30_000)])
+                                      ("f32", torch.float32, 30_000),
+                                      ("bf16", torch.bfloat16, 30_728)])
 def test_bwd_sweep_equals_row_kernel(dt, gdt, V):
     # wide rows on 4-byte boundaries take the backward as a sweep of 256-vector
     # pieces; the fused kernel's second pass and (for bf16) rows on 2-byte
