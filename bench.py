@@ -330,7 +330,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
-              "(rows shard across GPUs with no exchange, see the design notes)", file=sys.stderr)
+              "(rows shard across GPUs with no exchange: each GPU would run this path on its "
+              "own rows)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

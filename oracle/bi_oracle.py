@@ -36,8 +36,8 @@ F = set of columns with z_j > -inf, m = max_j z_j):
     entropy = -sum_{j in F} p_j ln p_j = ln S - U / S      (for every row)
     grad_j  = w * (p_j - [j == y]),  p_j = exp(z_j - lse)  (+0.0 rows when ignored)
 
-Readings taken where the pages are silent (each is listed with its reason in the
-design notes of the repository):
+Readings taken where the pages are silent (the plainest reading that the rest of
+the pages supports, each pinned by a test):
   * masked columns contribute 0 * ln 0 = 0 to the entropy (limit value);
   * ignored rows still get an entropy; their logprob and gradient are +0.0;
   * a label outside [0, V) that is not ignore_index yields NaN logprob and a
