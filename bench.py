@@ -240,6 +240,45 @@ def cpu_baseline(rows_total, sample_rows, seed):
                       f"{dt:.2f} s wall"}
 
 
+def generator_leg(bi, torch, np, logits, labels, trainer_logprob, seed, steps, warm, stream,
+                  k=8):
+    """The generator side on the large workload: K token ids per row sharing one lse
+    (the sampled label and K - 1 seeded candidates), then the trainer-vs-generator
+    difference metrics between its label column and the fused call's logprob."""
+    n, v = logits.shape
+    g = np.random.default_rng([seed, 31])
+    cand = torch.from_numpy(g.integers(0, v, size=(n, k), dtype=np.int64)).to(logits.device)
+    cand[:, 0] = labels
+
+    def timed(fn):
+        for _ in range(max(warm, 1)):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        outs = []
+        for e0, e1 in ev:
+            e0.record(stream)
+            outs.append(fn())
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev])), outs[-1]
+
+    ms_multi, (lp, _, _) = timed(lambda: bi.fwd_multi(logits, cand, stream=stream))
+    gen = lp[:, 0].contiguous()
+    ms_diff, d = timed(lambda: bi.diff_stats(trainer_logprob, gen, labels, stream=stream))
+    d = d.cpu().tolist()
+    nbytes = n * (v * 2 + k * 8 + k * 4 + 8)
+    gbps = nbytes / (ms_multi * 1e-3) / 1e9
+    return {"what": f"bi_logprob_fwd_multi: {k} token ids per row sharing one lse; "
+                    "bi_logprob_diff_stats between its label column and the fused call's "
+                    "logprob", "k": k, "ms": ms_multi, "rows_per_s": n / (ms_multi * 1e-3),
+            "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS, "traffic": None},
+            "diff_stats_ms": ms_diff,
+            "trainer_vs_generator": {"mean": d[0], "abs_mean": d[1], "max": d[2],
+                                     "frac_tokens_different": d[3]}}
+
+
 def configs_leg(bi, torch, np, wl, seed, steps, warm, stream, with_cpu=True):
     """The pages' other workload shapes (256 x 151,936 fp32 forward; 4,096 x 151,936
     bf16 and 2,048 x 151,937 masked fp32 forward + backward), all rows drawn as the
@@ -524,6 +563,10 @@ def main():
     if not args.no_lmhead:
         line["lmhead"] = lmhead_leg(bi, torch, np, wl, N, V, seed, steps, warm, stream,
                                     with_cpu=not args.no_cpu_baseline and not args.profile_steps)
+    if not args.profile_steps:
+        step_fused()     # lp: the trainer's logprob, from the fused call
+        line["generator"] = generator_leg(bi, torch, np, logits, labels, lp, seed, steps, warm,
+                                          stream)
     if not args.no_configs and not args.profile_steps:
         line["configs"] = configs_leg(bi, torch, np, wl, seed, steps, warm, stream,
                                       with_cpu=not args.no_cpu_baseline)
