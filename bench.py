@@ -550,6 +550,12 @@ def main():
                      "kernel": "fused fwd+bwd (bf16 logits, bf16 grad)",
                      "bytes_per_launch": kernels[dom]["bytes"]},
         "kernels": kernels,
+        "vs_target": {
+            "what": "70% of 8 TB/s over the two-pass algorithmic bytes of one step "
+                    "(forward read + backward read and write)",
+            "target_ms": N * (f_b + b_b) / (0.7 * HBM_PEAK_GBPS * 1e9) * 1e3,
+            "fused_step_speedup": N * (f_b + b_b) / (0.7 * HBM_PEAK_GBPS * 1e9) * 1e3 / ms_step,
+            "two_call_pct_hbm_peak": 100 * gbps(N * (f_b + b_b), ms_two) / HBM_PEAK_GBPS},
         "reference_copy": {
             "what": "torch.neg(logits, out=grad): a library copy of the same tensor, one read "
                     "and one write per element (the fused kernel's HBM bytes), same run",
