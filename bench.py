@@ -94,6 +94,33 @@ def measured_traffic(kernel, summary=TRAFFIC_SUMMARY, sources=KERNEL_SOURCES):
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
 
 
+def host_cpu():
+    """(cores this process may run on, oracle worker threads).  The threads are
+    capped at 16, the host share of one GPU on the boxes this runs on."""
+    import workloads as wl
+
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    return cores, wl.default_threads()
+
+
+def ceilings_lib():
+    """libbi_ceilings.so: a plain read-only stream and a plain copy (bench only)."""
+    import ctypes
+
+    path = os.path.join(ROOT, "entropy_bi_logprob_amd", "libbi_ceilings.so")
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build with `python -m entropy_bi_logprob_amd.build`")
+    L = ctypes.CDLL(path)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    L.bi_ceiling_read.argtypes = [vp, i64, vp, vp]
+    L.bi_ceiling_copy.argtypes = [vp, vp, i64, vp]
+    L.bi_ceiling_read.restype = L.bi_ceiling_copy.restype = ctypes.c_int
+    return L
+
+
 def lmhead_leg(bi, torch, np, wl, N, V, seed, steps, warm, stream, with_cpu=True):
     """Logprob/entropy straight from hidden states: hidden [N, 2560] x lm_head [V, 2560]^T
     on the matrix cores, reduced to statistics without materialising the logits; timed
@@ -204,8 +231,11 @@ def lmhead_cpu_baseline(b, np, wl, sample=2048):
     t1 = time.perf_counter()
     orc.lmhead_backward(h, w, labels, lse, np.full(sample, -1.0 / sample))
     t2 = time.perf_counter()
+    cores, _ = host_cpu()
+    blas = os.environ.get("OMP_NUM_THREADS", "unset")
     return {"fwd_tokens_per_s": sample / (t1 - t0), "fwd_bwd_tokens_per_s": sample / (t2 - t0),
-            "unit": "tokens/s", "cores": wl.default_threads(), "kind": "oracle",
+            "unit": "tokens/s", "cores": cores, "threads": f"BLAS threads (OMP_NUM_THREADS={blas})",
+            "kind": "oracle",
             "sample": f"{sample} tokens x 151936 lm_head rows x d 2560, fp64 numpy "
                       f"(BLAS threads as configured), {t2 - t0:.1f} s wall"}
 
@@ -222,7 +252,7 @@ def cpu_baseline(rows_total, sample_rows, seed):
     g = np.random.default_rng([seed, 77])
     rows = np.sort(g.choice(rows_total, size=sample_rows, replace=False))
     b = wl.draw(5, rows=rows, seed=seed)
-    threads = wl.default_threads()
+    cores, threads = host_cpu()
     block = 16
 
     def run(a):
@@ -234,10 +264,12 @@ def cpu_baseline(rows_total, sample_rows, seed):
     with ThreadPoolExecutor(threads) as ex:
         list(ex.map(run, range(0, sample_rows, block)))
     dt = time.perf_counter() - t0
-    return {"value": sample_rows / dt, "unit": "rows/s", "cores": threads, "kind": "oracle",
+    return {"value": sample_rows / dt, "unit": "rows/s", "cores": cores, "threads": threads,
+            "kind": "oracle",
             "sample": f"{sample_rows} seeded rows of the 32768x151936 bf16 workload, "
-                      f"fp64 numpy forward+backward, {threads} threads over 16-row blocks, "
-                      f"{dt:.2f} s wall"}
+                      f"fp64 numpy forward+backward, {threads} worker threads (capped at the "
+                      f"16-core host share of one GPU) over 16-row blocks on a host with "
+                      f"{cores} cores available, {dt:.2f} s wall"}
 
 
 def generator_leg(bi, torch, np, logits, labels, trainer_logprob, seed, steps, warm, stream,
@@ -345,7 +377,8 @@ def configs_leg(bi, torch, np, wl, seed, steps, warm, stream, with_cpu=True):
         if with_cpu:
             import oracle.bi_oracle as orc
 
-            threads, block = wl.default_threads(), 16
+            cores, threads = host_cpu()
+            block = 16
 
             def run(a):
                 z = orc.decode(b.logits[a:a + block], w.dtype)
@@ -358,8 +391,8 @@ def configs_leg(bi, torch, np, wl, seed, steps, warm, stream, with_cpu=True):
             with ThreadPoolExecutor(threads) as ex:
                 list(ex.map(run, range(0, w.rows, block)))
             dt = time.perf_counter() - t0
-            res["cpu_oracle"] = {"rows_per_s": w.rows / dt, "cores": threads, "s": dt,
-                                 "sample": "all rows, fp64 numpy, 16-row blocks"}
+            res["cpu_oracle"] = {"rows_per_s": w.rows / dt, "cores": cores, "threads": threads,
+                                 "s": dt, "sample": "all rows, fp64 numpy, 16-row blocks"}
         out[w.name] = res
         del logits, grad
     return out
@@ -494,6 +527,31 @@ def main():
     step_copy()
     _, (t_copy,) = timed(step_copy, 2)
 
+    # same-run ceilings: a plain read-only stream over the logits and a plain
+    # copy of the logits into the gradient buffer (libbi_ceilings.so)
+    CL = ceilings_lib()
+    nbytes_logits = N * V * 2
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+
+    def step_read(ev=None):
+        if ev: ev[0].record(stream)
+        rc = CL.bi_ceiling_read(logits.data_ptr(), nbytes_logits, sink.data_ptr(),
+                                stream.cuda_stream)
+        assert rc == 0, rc
+        if ev: ev[1].record(stream)
+
+    def step_plain_copy(ev=None):
+        if ev: ev[0].record(stream)
+        rc = CL.bi_ceiling_copy(logits.data_ptr(), grad.data_ptr(), nbytes_logits,
+                                stream.cuda_stream)
+        assert rc == 0, rc
+        if ev: ev[1].record(stream)
+
+    step_read()
+    step_plain_copy()
+    _, (t_read,) = timed(step_read, 2)
+    _, (t_pcopy,) = timed(step_plain_copy, 2)
+
     f_b, b_b, c_b, m_b = algorithmic_bytes(V, 2, 2, len(bounds))
     fused_b = V * (2 + 2) + 8 + 4 + 12       # one read of the logits, one write of the grad
     med = lambda xs: float(np.median(xs))
@@ -512,8 +570,22 @@ def main():
                            "bytes": N * c_b},
         "combine": {"ms": mean(t_comb), "GBps": gbps(N * m_b, mean(t_comb)), "bytes": N * m_b},
     }
-    for k in kernels.values():
+    read_ceiling = gbps(nbytes_logits, mean(t_read))
+    copy_ceiling = gbps(2 * nbytes_logits, mean(t_pcopy))
+    ceilings = {"what": "same run, same tensors: a plain read-only stream of the logits and "
+                        "a plain copy of the logits into the gradient buffer (256-lane "
+                        "workgroups, 16-byte non-temporal loads and stores)",
+                "read_GBps": read_ceiling, "copy_GBps": copy_ceiling,
+                "read_ms": mean(t_read), "copy_ms": mean(t_pcopy),
+                "read_frac_of_peak": read_ceiling / HBM_PEAK_GBPS,
+                "copy_frac_of_peak": copy_ceiling / HBM_PEAK_GBPS}
+    # the ceiling each kernel is held to: reads only (forward, chunk statistics)
+    # or a read and a write per element (backward, fused)
+    ceiling_of = {"fused": copy_ceiling, "fwd": read_ceiling, "bwd": copy_ceiling,
+                  "chunk_stats_x4": read_ceiling, "combine": read_ceiling}
+    for name, k in kernels.items():
         k["frac_of_peak"] = k["GBps"] / HBM_PEAK_GBPS
+        k["frac_of_ceiling"] = k["GBps"] / ceiling_of[name]
     dom = "fused"
     two_call = {"ms_per_step": ms_two, "rows_per_s": N / (ms_two * 1e-3),
                 "hbm_GBps": gbps(N * (f_b + b_b), ms_two),
@@ -536,10 +608,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "large_32768x151936_bf16", "rows": N, "vocab": V,
-                   "logits_dtype": "bf16", "grad_dtype": "bf16",
+                   "logits_dtype": "bf16", "grad_dtype": "bf16", "accum_dtype": "f32",
                    "path": "bi_logprob_fwd_bwd (full-row fwd + bwd, one call)", "seed": seed},
         "logits_GBps": N * V * 2 / (ms_step * 1e-3) / 1e9,
         "hbm_GBps": hbm,
@@ -551,11 +623,19 @@ def main():
                      "bytes_per_launch": kernels[dom]["bytes"]},
         "kernels": kernels,
         "vs_target": {
-            "what": "70% of 8 TB/s over the two-pass algorithmic bytes of one step "
-                    "(forward read + backward read and write)",
+            "what": "the target is 70% of 8 TB/s.  On its own bytes (one read of the logits, "
+                    "one write of the gradient) the fused kernel reaches "
+                    "fused_kernel_frac_of_peak; the two-call path reaches "
+                    "two_call_pct_hbm_peak on its two-pass bytes.  Context only: "
+                    "target_ms is 70% of peak over the two-pass bytes, which the fused "
+                    "kernel does not move",
+            "fused_kernel_frac_of_peak": kernels[dom]["GBps"] / HBM_PEAK_GBPS,
+            "fused_kernel_frac_of_copy_ceiling": kernels[dom]["frac_of_ceiling"],
+            "two_call_pct_hbm_peak": 100 * gbps(N * (f_b + b_b), ms_two) / HBM_PEAK_GBPS,
             "target_ms": N * (f_b + b_b) / (0.7 * HBM_PEAK_GBPS * 1e9) * 1e3,
-            "fused_step_speedup": N * (f_b + b_b) / (0.7 * HBM_PEAK_GBPS * 1e9) * 1e3 / ms_step,
-            "two_call_pct_hbm_peak": 100 * gbps(N * (f_b + b_b), ms_two) / HBM_PEAK_GBPS},
+            "fused_step_vs_two_pass_target": N * (f_b + b_b) / (0.7 * HBM_PEAK_GBPS * 1e9) * 1e3
+            / ms_step},
+        "ceilings": ceilings,
         "reference_copy": {
             "what": "torch.neg(logits, out=grad): a library copy of the same tensor, one read "
                     "and one write per element (the fused kernel's HBM bytes), same run",

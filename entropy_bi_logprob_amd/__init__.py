@@ -14,6 +14,7 @@ exactly (sections Summary, Why, Correctness and compatibility).
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import Optional, Tuple
@@ -166,10 +167,23 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _stream(stream) -> ctypes.c_void_p:
+@contextlib.contextmanager
+def _on_stream(stream):
+    """Make ``stream`` (torch's current stream when None; a torch stream or a raw
+    hipStream_t) current while a wrapper allocates, fills and launches, and yield
+    its handle.  Tensors the wrapper allocates (outputs, a zero-filled
+    grad_hidden, workspaces and intermediate statistics) then belong to that
+    stream: their fills are ordered before the library's kernels, and the
+    caching allocator hands their memory to other work only after everything
+    queued on that stream before the release."""
     if stream is None:
-        stream = torch.cuda.current_stream()
-    return ctypes.c_void_p(int(getattr(stream, "cuda_stream", stream)))
+        s = torch.cuda.current_stream()
+    elif isinstance(stream, torch.cuda.Stream):
+        s = stream
+    else:
+        s = torch.cuda.ExternalStream(int(getattr(stream, "cuda_stream", stream)))
+    with torch.cuda.stream(s):
+        yield ctypes.c_void_p(s.cuda_stream)
 
 
 # ------------------------------------------------------------------ entry points
@@ -180,13 +194,15 @@ def fwd(logits: torch.Tensor, labels: torch.Tensor, ignore_index: int = IGNORE_I
     """(logprob, entropy, lse) fp32 [N] for full rows of ``logits`` [N, V]."""
     n, v, rs = _rows(logits, "logits")
     _vec(labels, n, torch.int64, "labels")
-    if out is None:
-        out = tuple(torch.empty(n, dtype=torch.float32, device=logits.device) for _ in range(3))
-    lp, ent, lse = (_vec(o, n, torch.float32, "out") for o in out)
     _vec(status, 1, torch.int32, "status")
-    _check("bi_logprob_fwd", lib().bi_logprob_fwd(
-        _ptr(logits), _dtype_code(logits.dtype), n, v, rs, _ptr(labels), ignore_index,
-        _ptr(lp), _ptr(ent), _ptr(lse), _ptr(status), _stream(stream)))
+    with _on_stream(stream) as hs:
+        if out is None:
+            out = tuple(torch.empty(n, dtype=torch.float32, device=logits.device)
+                        for _ in range(3))
+        lp, ent, lse = (_vec(o, n, torch.float32, "out") for o in out)
+        _check("bi_logprob_fwd", lib().bi_logprob_fwd(
+            _ptr(logits), _dtype_code(logits.dtype), n, v, rs, _ptr(labels), ignore_index,
+            _ptr(lp), _ptr(ent), _ptr(lse), _ptr(status), hs))
     return lp, ent, lse
 
 
@@ -200,15 +216,15 @@ def bwd(logits: torch.Tensor, labels: torch.Tensor, lse: torch.Tensor,
     _vec(lse, n, torch.float32, "lse")
     _vec(weights, n, torch.float32, "weights")
     _vec(status, 1, torch.int32, "status")
-    if out is None:
-        out = torch.empty((n, v), dtype=grad_dtype or logits.dtype, device=logits.device)
-    gn, gv, grs = _rows(out, "grad")
-    if (gn, gv) != (n, v):
-        raise ValueError("grad must have the logits' shape")
-    _check("bi_logprob_bwd", lib().bi_logprob_bwd(
-        _ptr(logits), _dtype_code(logits.dtype), n, v, rs, _ptr(labels), ignore_index,
-        _ptr(lse), _ptr(weights), _ptr(out), _dtype_code(out.dtype), grs, _ptr(status),
-        _stream(stream)))
+    with _on_stream(stream) as hs:
+        if out is None:
+            out = torch.empty((n, v), dtype=grad_dtype or logits.dtype, device=logits.device)
+        gn, gv, grs = _rows(out, "grad")
+        if (gn, gv) != (n, v):
+            raise ValueError("grad must have the logits' shape")
+        _check("bi_logprob_bwd", lib().bi_logprob_bwd(
+            _ptr(logits), _dtype_code(logits.dtype), n, v, rs, _ptr(labels), ignore_index,
+            _ptr(lse), _ptr(weights), _ptr(out), _dtype_code(out.dtype), grs, _ptr(status), hs))
     return out
 
 
@@ -224,18 +240,20 @@ def fwd_bwd(logits: torch.Tensor, labels: torch.Tensor, weights: Optional[torch.
     _vec(labels, n, torch.int64, "labels")
     _vec(weights, n, torch.float32, "weights")
     _vec(status, 1, torch.int32, "status")
-    if out is None:
-        out = tuple(torch.empty(n, dtype=torch.float32, device=logits.device) for _ in range(3))
-    lp, ent, lse = (_vec(o, n, torch.float32, "out") for o in out)
-    if grad is None:
-        grad = torch.empty((n, v), dtype=grad_dtype or logits.dtype, device=logits.device)
-    gn, gv, grs = _rows(grad, "grad")
-    if (gn, gv) != (n, v):
-        raise ValueError("grad must have the logits' shape")
-    _check("bi_logprob_fwd_bwd", lib().bi_logprob_fwd_bwd(
-        _ptr(logits), _dtype_code(logits.dtype), n, v, rs, _ptr(labels), ignore_index,
-        _ptr(weights), _ptr(lp), _ptr(ent), _ptr(lse), _ptr(grad), _dtype_code(grad.dtype), grs,
-        _ptr(status), _stream(stream)))
+    with _on_stream(stream) as hs:
+        if out is None:
+            out = tuple(torch.empty(n, dtype=torch.float32, device=logits.device)
+                        for _ in range(3))
+        lp, ent, lse = (_vec(o, n, torch.float32, "out") for o in out)
+        if grad is None:
+            grad = torch.empty((n, v), dtype=grad_dtype or logits.dtype, device=logits.device)
+        gn, gv, grs = _rows(grad, "grad")
+        if (gn, gv) != (n, v):
+            raise ValueError("grad must have the logits' shape")
+        _check("bi_logprob_fwd_bwd", lib().bi_logprob_fwd_bwd(
+            _ptr(logits), _dtype_code(logits.dtype), n, v, rs, _ptr(labels), ignore_index,
+            _ptr(weights), _ptr(lp), _ptr(ent), _ptr(lse), _ptr(grad), _dtype_code(grad.dtype),
+            grs, _ptr(status), hs))
     return lp, ent, lse, grad
 
 
@@ -256,18 +274,20 @@ def policy_loss_fwd_bwd(logits: torch.Tensor, labels: torch.Tensor, old_logprob:
     _vec(advantages, n, torch.float32, "advantages")
     _vec(loss_scale, n, torch.float32, "loss_scale")
     _vec(status, 1, torch.int32, "status")
-    outs = tuple(torch.empty(n, dtype=torch.float32, device=logits.device) for _ in range(5))
-    if grad is None:
-        grad = torch.empty((n, v), dtype=grad_dtype or logits.dtype, device=logits.device)
-    gn, gv, grs = _rows(grad, "grad")
-    if (gn, gv) != (n, v):
-        raise ValueError("grad must have the logits' shape")
-    lp, ent, lse, loss, w = outs
-    _check("bi_policy_loss_fwd_bwd", lib().bi_policy_loss_fwd_bwd(
-        _ptr(logits), _dtype_code(logits.dtype), n, v, rs, _ptr(labels), ignore_index,
-        _ptr(old_logprob), _ptr(advantages), _ptr(loss_scale), float(clip_low), float(clip_high),
-        _ptr(lp), _ptr(ent), _ptr(lse), _ptr(loss), _ptr(w), _ptr(grad), _dtype_code(grad.dtype),
-        grs, _ptr(status), _stream(stream)))
+    with _on_stream(stream) as hs:
+        outs = tuple(torch.empty(n, dtype=torch.float32, device=logits.device)
+                     for _ in range(5))
+        if grad is None:
+            grad = torch.empty((n, v), dtype=grad_dtype or logits.dtype, device=logits.device)
+        gn, gv, grs = _rows(grad, "grad")
+        if (gn, gv) != (n, v):
+            raise ValueError("grad must have the logits' shape")
+        lp, ent, lse, loss, w = outs
+        _check("bi_policy_loss_fwd_bwd", lib().bi_policy_loss_fwd_bwd(
+            _ptr(logits), _dtype_code(logits.dtype), n, v, rs, _ptr(labels), ignore_index,
+            _ptr(old_logprob), _ptr(advantages), _ptr(loss_scale), float(clip_low),
+            float(clip_high), _ptr(lp), _ptr(ent), _ptr(lse), _ptr(loss), _ptr(w), _ptr(grad),
+            _dtype_code(grad.dtype), grs, _ptr(status), hs))
     return lp, ent, lse, loss, w, grad
 
 
@@ -286,13 +306,14 @@ def vocab_chunk_stats(logits_chunk: torch.Tensor, labels: torch.Tensor, vocab_of
     n, w, rs = _rows(logits_chunk, "logits_chunk")
     _vec(labels, n, torch.int64, "labels")
     _vec(status, 1, torch.int32, "status")
-    if out is None:
-        out = torch.empty((n, 4), dtype=torch.float32, device=logits_chunk.device)
-    if out.shape != (n, 4) or out.dtype != torch.float32 or not out.is_contiguous():
-        raise ValueError("out must be a contiguous float32 [N, 4] tensor")
-    _check("bi_vocab_chunk_stats", lib().bi_vocab_chunk_stats(
-        _ptr(logits_chunk), _dtype_code(logits_chunk.dtype), n, w, rs, vocab_offset, vocab,
-        _ptr(labels), ignore_index, _ptr(out), _ptr(status), _stream(stream)))
+    with _on_stream(stream) as hs:
+        if out is None:
+            out = torch.empty((n, 4), dtype=torch.float32, device=logits_chunk.device)
+        if out.shape != (n, 4) or out.dtype != torch.float32 or not out.is_contiguous():
+            raise ValueError("out must be a contiguous float32 [N, 4] tensor")
+        _check("bi_vocab_chunk_stats", lib().bi_vocab_chunk_stats(
+            _ptr(logits_chunk), _dtype_code(logits_chunk.dtype), n, w, rs, vocab_offset, vocab,
+            _ptr(labels), ignore_index, _ptr(out), _ptr(status), hs))
     return out
 
 
@@ -304,12 +325,13 @@ def stats_combine(stats: torch.Tensor, labels: torch.Tensor, ignore_index: int =
         raise ValueError("stats must be a contiguous device float32 [C, N, 4] tensor")
     c, n, _ = stats.shape
     _vec(labels, n, torch.int64, "labels")
-    if out is None:
-        out = tuple(torch.empty(n, dtype=torch.float32, device=stats.device) for _ in range(3))
-    lp, ent, lse = (_vec(o, n, torch.float32, "out") for o in out)
-    _check("bi_stats_combine", lib().bi_stats_combine(
-        _ptr(stats), c, n, _ptr(labels), ignore_index, _ptr(lp), _ptr(ent), _ptr(lse),
-        _stream(stream)))
+    with _on_stream(stream) as hs:
+        if out is None:
+            out = tuple(torch.empty(n, dtype=torch.float32, device=stats.device)
+                        for _ in range(3))
+        lp, ent, lse = (_vec(o, n, torch.float32, "out") for o in out)
+        _check("bi_stats_combine", lib().bi_stats_combine(
+            _ptr(stats), c, n, _ptr(labels), ignore_index, _ptr(lp), _ptr(ent), _ptr(lse), hs))
     return lp, ent, lse
 
 
@@ -322,13 +344,14 @@ def fwd_multi(logits: torch.Tensor, labels: torch.Tensor, ignore_index: int = IG
         raise ValueError("labels must be a device int64 [N, K] tensor, last dim contiguous")
     k = labels.shape[1]
     _vec(status, 1, torch.int32, "status")
-    lp = torch.empty((n, k), dtype=torch.float32, device=logits.device)
-    ent = torch.empty(n, dtype=torch.float32, device=logits.device)
-    lse = torch.empty(n, dtype=torch.float32, device=logits.device)
     ls = labels.stride(0) if n > 1 else k
-    _check("bi_logprob_fwd_multi", lib().bi_logprob_fwd_multi(
-        _ptr(logits), _dtype_code(logits.dtype), n, v, rs, _ptr(labels), ls, k, ignore_index,
-        _ptr(lp), _ptr(ent), _ptr(lse), _ptr(status), _stream(stream)))
+    with _on_stream(stream) as hs:
+        lp = torch.empty((n, k), dtype=torch.float32, device=logits.device)
+        ent = torch.empty(n, dtype=torch.float32, device=logits.device)
+        lse = torch.empty(n, dtype=torch.float32, device=logits.device)
+        _check("bi_logprob_fwd_multi", lib().bi_logprob_fwd_multi(
+            _ptr(logits), _dtype_code(logits.dtype), n, v, rs, _ptr(labels), ls, k, ignore_index,
+            _ptr(lp), _ptr(ent), _ptr(lse), _ptr(status), hs))
     return lp, ent, lse
 
 
@@ -339,9 +362,10 @@ def diff_stats(a: torch.Tensor, b: torch.Tensor, labels: Optional[torch.Tensor] 
     _vec(a, n, torch.float32, "a")
     _vec(b, n, torch.float32, "b")
     _vec(labels, n, torch.int64, "labels")
-    out = torch.empty(4, dtype=torch.float32, device=a.device)
-    _check("bi_logprob_diff_stats", lib().bi_logprob_diff_stats(
-        _ptr(a), _ptr(b), _ptr(labels), ignore_index, n, _ptr(out), _stream(stream)))
+    with _on_stream(stream) as hs:
+        out = torch.empty(4, dtype=torch.float32, device=a.device)
+        _check("bi_logprob_diff_stats", lib().bi_logprob_diff_stats(
+            _ptr(a), _ptr(b), _ptr(labels), ignore_index, n, _ptr(out), hs))
     return out
 
 
@@ -364,13 +388,14 @@ def lmhead_tile_stats(hidden: torch.Tensor, weight: torch.Tensor, labels: torch.
     _vec(status, 1, torch.int32, "status")
     vocab = vocab_offset + vc if vocab is None else vocab
     tiles = int(lib().bi_lmhead_tiles(vc))
-    if out is None:
-        out = torch.empty((tiles, n, 4), dtype=torch.float32, device=hidden.device)
-    if out.shape != (tiles, n, 4) or out.dtype != torch.float32 or not out.is_contiguous():
-        raise ValueError(f"out must be a contiguous float32 [{tiles}, {n}, 4] tensor")
-    _check("bi_lmhead_tile_stats", lib().bi_lmhead_tile_stats(
-        _ptr(hidden), _ptr(weight), n, vc, d, ldh, ldw, vocab_offset, vocab, _ptr(labels),
-        ignore_index, _ptr(out), _ptr(status), _stream(stream)))
+    with _on_stream(stream) as hs:
+        if out is None:
+            out = torch.empty((tiles, n, 4), dtype=torch.float32, device=hidden.device)
+        if out.shape != (tiles, n, 4) or out.dtype != torch.float32 or not out.is_contiguous():
+            raise ValueError(f"out must be a contiguous float32 [{tiles}, {n}, 4] tensor")
+        _check("bi_lmhead_tile_stats", lib().bi_lmhead_tile_stats(
+            _ptr(hidden), _ptr(weight), n, vc, d, ldh, ldw, vocab_offset, vocab, _ptr(labels),
+            ignore_index, _ptr(out), _ptr(status), hs))
     return out
 
 
@@ -382,9 +407,12 @@ def lmhead_tile_rows() -> int:
 def lmhead_logprob(hidden: torch.Tensor, weight: torch.Tensor, labels: torch.Tensor,
                    ignore_index: int = IGNORE_INDEX, status=None, stream=None):
     """(logprob, entropy, lse) of the logits hidden @ weight^T without materialising them."""
-    st = lmhead_tile_stats(hidden, weight, labels, 0, weight.shape[0], ignore_index,
-                           status=status, stream=stream)
-    return stats_combine(st, labels, ignore_index, stream=stream)
+    with _on_stream(stream):
+        # the intermediate statistics belong to the launch stream: their memory
+        # is reused only after the combine that reads them
+        st = lmhead_tile_stats(hidden, weight, labels, 0, weight.shape[0], ignore_index,
+                               status=status, stream=stream)
+        return stats_combine(st, labels, ignore_index, stream=stream)
 
 
 def _lmhead_operands(hidden, weight, labels):
@@ -408,15 +436,15 @@ def lmhead_grad_logits(hidden: torch.Tensor, weight: torch.Tensor, labels: torch
     _vec(token_weights, n, torch.float32, "token_weights")
     _vec(status, 1, torch.int32, "status")
     vocab = vocab_offset + vc if vocab is None else vocab
-    if out is None:
-        out = torch.empty((vc, n), dtype=torch.bfloat16, device=hidden.device)
-    _, ncols, ldg = _rows(out, "out")
-    if out.dtype != torch.bfloat16 or out.shape[0] != vc or ncols != n:
-        raise ValueError(f"out must be a bfloat16 [{vc}, {n}] tensor")
-    _check("bi_lmhead_grad_logits", lib().bi_lmhead_grad_logits(
-        _ptr(hidden), _ptr(weight), n, vc, d, ldh, ldw, vocab_offset, vocab, _ptr(labels),
-        ignore_index, _ptr(lse), _ptr(token_weights), _ptr(out), ldg, _ptr(status),
-        _stream(stream)))
+    with _on_stream(stream) as hs:
+        if out is None:
+            out = torch.empty((vc, n), dtype=torch.bfloat16, device=hidden.device)
+        _, ncols, ldg = _rows(out, "out")
+        if out.dtype != torch.bfloat16 or out.shape[0] != vc or ncols != n:
+            raise ValueError(f"out must be a bfloat16 [{vc}, {n}] tensor")
+        _check("bi_lmhead_grad_logits", lib().bi_lmhead_grad_logits(
+            _ptr(hidden), _ptr(weight), n, vc, d, ldh, ldw, vocab_offset, vocab, _ptr(labels),
+            ignore_index, _ptr(lse), _ptr(token_weights), _ptr(out), ldg, _ptr(status), hs))
     return out
 
 
@@ -436,25 +464,28 @@ def lmhead_backward(hidden: torch.Tensor, weight: torch.Tensor, labels: torch.Te
     _vec(status, 1, torch.int32, "status")
     vocab = vocab_offset + vc if vocab is None else vocab
     dev = hidden.device
-    if grad_hidden is None:
-        grad_hidden = torch.zeros((n, d), dtype=torch.float32, device=dev)
-    _, dh, ldgh = _rows(grad_hidden, "grad_hidden")
-    if grad_hidden.dtype != torch.float32 or grad_hidden.shape[0] != n or dh != d:
-        raise ValueError(f"grad_hidden must be a float32 [{n}, {d}] tensor")
-    if grad_weight is None:
-        grad_weight = torch.empty((vc, d), dtype=grad_weight_dtype, device=dev)
-    _, dgw, ldgw = _rows(grad_weight, "grad_weight")
-    if grad_weight.shape[0] != vc or dgw != d:
-        raise ValueError(f"grad_weight must be a [{vc}, {d}] tensor")
     L = lib()
-    if workspace is None:
-        nbytes = int(L.bi_lmhead_backward_workspace(n, d, min(chunk_rows, max(vc, 1))))
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    _check("bi_lmhead_backward", L.bi_lmhead_backward(
-        _ptr(hidden), _ptr(weight), n, vc, d, ldh, ldw, vocab_offset, vocab, _ptr(labels),
-        ignore_index, _ptr(lse), _ptr(token_weights), _ptr(grad_hidden), ldgh,
-        _ptr(grad_weight), _dtype_code(grad_weight.dtype), ldgw, _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _ptr(status), _stream(stream)))
+    with _on_stream(stream) as hs:
+        # a fresh grad_hidden is zero-filled on the launch stream, ahead of the
+        # kernels that accumulate into it; the workspace belongs to that stream
+        if grad_hidden is None:
+            grad_hidden = torch.zeros((n, d), dtype=torch.float32, device=dev)
+        _, dh, ldgh = _rows(grad_hidden, "grad_hidden")
+        if grad_hidden.dtype != torch.float32 or grad_hidden.shape[0] != n or dh != d:
+            raise ValueError(f"grad_hidden must be a float32 [{n}, {d}] tensor")
+        if grad_weight is None:
+            grad_weight = torch.empty((vc, d), dtype=grad_weight_dtype, device=dev)
+        _, dgw, ldgw = _rows(grad_weight, "grad_weight")
+        if grad_weight.shape[0] != vc or dgw != d:
+            raise ValueError(f"grad_weight must be a [{vc}, {d}] tensor")
+        if workspace is None:
+            nbytes = int(L.bi_lmhead_backward_workspace(n, d, min(chunk_rows, max(vc, 1))))
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        _check("bi_lmhead_backward", L.bi_lmhead_backward(
+            _ptr(hidden), _ptr(weight), n, vc, d, ldh, ldw, vocab_offset, vocab, _ptr(labels),
+            ignore_index, _ptr(lse), _ptr(token_weights), _ptr(grad_hidden), ldgh,
+            _ptr(grad_weight), _dtype_code(grad_weight.dtype), ldgw, _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _ptr(status), hs))
     return grad_hidden, grad_weight
 
 

@@ -1,4 +1,6 @@
-"""Build libbi_logprob.so (HIP, gfx950) in-tree with hipcc.
+"""Build libbi_logprob.so (HIP, gfx950) in-tree with hipcc, and beside it
+libbi_ceilings.so (two plain streaming kernels the benchmark uses to measure
+the HBM read and copy ceilings in the same run).
 
     python -m entropy_bi_logprob_amd.build
 
@@ -21,6 +23,8 @@ SOURCES = [os.path.join(PKG, "csrc", f)
 LIBS = ["-L/opt/rocm/lib", "-lhipblaslt"]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libbi_logprob.so")
+CEILINGS_SOURCES = [os.path.join(PKG, "csrc", "bi_ceilings.hip")]
+CEILINGS_LIB = os.path.join(PKG, "libbi_ceilings.so")
 ARCH = "gfx950"
 
 # -ffp-contract=off: every multiply-add is written out explicitly in the
@@ -42,9 +46,16 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False, extra_flags=(), out: str = LIB) -> str:
-    """Compile the HIP library into ``out``; returns its path."""
+    """Compile the HIP library into ``out`` (and the ceilings library beside the
+    default one); returns the library's path."""
+    if out == LIB:
+        _compile(verbose, (), CEILINGS_LIB, CEILINGS_SOURCES, [])
+    return _compile(verbose, extra_flags, out, SOURCES, LIBS)
+
+
+def _compile(verbose, extra_flags, out, sources, libs) -> str:
     tmp = out + ".tmp"
-    cmd = [hipcc(), *FLAGS, *extra_flags, "-I", INCLUDE, "-o", tmp, *SOURCES, *LIBS]
+    cmd = [hipcc(), *FLAGS, *extra_flags, "-I", INCLUDE, "-o", tmp, *sources, *libs]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -69,3 +69,27 @@ def test_traffic_is_reported_only_for_the_sources_it_was_taken_from(tmp_path):
     # an unknown kernel or a missing summary gives no figure either
     assert bench.measured_traffic("no_such_kernel") is None
     assert bench.measured_traffic("fused", summary=str(tmp_path / "missing.md")) is None
+
+
+def test_cpu_baseline_reports_host_cores_and_threads_separately():
+    cores, threads = bench.host_cpu()
+    assert cores == len(os.sched_getaffinity(0))
+    assert 1 <= threads <= min(cores, 16)
+
+
+def test_ceilings_library_exports_and_validates():
+    # the same-run read and copy ceilings come from libbi_ceilings.so; its host
+    # checks reject bad arguments before anything is launched (no GPU here)
+    import ctypes
+    import pytest
+    path = os.path.join(ROOT, "entropy_bi_logprob_amd", "libbi_ceilings.so")
+    if not os.path.exists(path):
+        pytest.skip("libbi_ceilings.so not built")
+    L = bench.ceilings_lib()
+    P = ctypes.c_void_p(0x10000)
+    assert L.bi_ceiling_read(P, 100, P, None) == -1          # not a multiple of 16
+    assert L.bi_ceiling_read(None, 160, P, None) == -1       # no source
+    assert L.bi_ceiling_read(ctypes.c_void_p(0x10004), 160, P, None) == -1   # misaligned
+    assert L.bi_ceiling_copy(P, None, 160, None) == -1
+    assert L.bi_ceiling_copy(P, P, -16, None) == -1
+    assert L.bi_ceiling_read(P, 0, P, None) == 0             # nothing to do

@@ -69,3 +69,26 @@ def test_two_threads_two_streams():
         t.join(timeout=120)
     assert not any(t.is_alive() for t in threads), "a worker thread did not finish"
     assert not errors, errors
+
+
+@pytest.mark.parametrize("handle", [False, True], ids=["torch_stream", "raw_handle"])
+def test_explicit_side_stream(handle):
+    # every wrapper given stream= a side stream (not torch's current one): the
+    # outputs, the zero-filled grad_hidden, the lm_head backward's workspace and
+    # the lm_head statistics it allocates belong to that stream, so churning the
+    # allocator on the current stream meanwhile changes nothing
+    case = make_case(81)
+    ref = run(case)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    arg = s.cuda_stream if handle else s
+    lp, ent, lse, grad = bi.fwd_bwd(case["z"], case["y"], case["w"], stream=arg)
+    hlp, hent, hlse = bi.lmhead_logprob(case["H"], case["W"], case["hy"], stream=arg)
+    gh, gw = bi.lmhead_backward(case["H"], case["W"], case["hy"], hlse, case["tw"],
+                                chunk_rows=512, stream=arg)
+    junk = [torch.full((1 << 22,), float(i), device="cuda") for i in range(16)]
+    del junk
+    s.synchronize()
+    outs = [lp, ent, lse, grad, hlp, hent, hlse, gh, gw]
+    for k, (o, r) in enumerate(zip(outs, ref)):
+        assert same(o, r), f"output {k} differs on a side stream"
