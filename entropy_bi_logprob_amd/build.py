@@ -5,8 +5,7 @@ the HBM read and copy ceilings in the same run).
     python -m entropy_bi_logprob_amd.build
 
 The library is a plain C ABI (include/bi_logprob.h) around hand-written HIP
-kernels; it links the HIP runtime and hipBLASLt (the lm_head backward's two
-plain GEMMs).
+kernels; it links only the HIP runtime.
 """
 from __future__ import annotations
 
@@ -19,8 +18,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SOURCES = [os.path.join(PKG, "csrc", f)
            for f in ("bi_logprob.hip", "bi_lmhead.hip", "bi_lmhead_bwd.hip")]
-# the lm_head backward's two plain GEMMs are hipBLASLt calls
-LIBS = ["-L/opt/rocm/lib", "-lhipblaslt"]
+LIBS = []
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libbi_logprob.so")
 CEILINGS_SOURCES = [os.path.join(PKG, "csrc", "bi_ceilings.hip")]

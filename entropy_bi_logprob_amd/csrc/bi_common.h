@@ -30,12 +30,14 @@ bool aligned(const void* p, size_t a);
 int launched(const char* what);
 const char* last_error();
 
-// D[i][j] = sum_k A[i][k] B[j][k] (bf16 operands with rows of k contiguous
-// elements, fp32 accumulation; D fp32 or bf16) on the lm_head kernel's
-// matrix-core pipeline, queued on `stream`.  Used by the lm_head backward.
-int lmhead_product(const char* fn, const void* a, int64_t a_rows, int64_t lda, const void* b,
-                   int64_t b_rows, int64_t ldb, int64_t k, void* d, int64_t ldd, bool d_bf16,
-                   bi_stream_t stream);
+// D[i][j] = sum_k A[i][k] B[k][j] on the lm_head kernel's matrix-core
+// pipeline: A [m][k] bf16 with rows of k contiguous elements (zero in its
+// columns kvalid_b .. k-1), B [k][n] bf16 with rows of n contiguous elements,
+// of which rows kvalid_b .. k-1 (fewer than 64) are read as its last one; k a
+// multiple of 64; D fp32 or bf16, overwritten.  Used by the lm_head backward.
+int lmhead_product_nt(const char* fn, const void* a, int64_t m, int64_t lda, const void* b,
+                      int64_t n, int64_t ldb, int64_t k, int64_t kvalid_b, void* d, int64_t ldd,
+                      bool d_bf16, bi_stream_t stream);
 
 // D[i][j] += sum_k A[k][i] B[k][j] on the same pipeline with transposing LDS
 // reads: A [k][m] and B [k][n] bf16 with rows of m (n) contiguous elements; k
@@ -45,15 +47,16 @@ int lmhead_product_t(const char* fn, const void* a, int64_t m, int64_t lda, cons
                      int64_t n, int64_t ldb, int64_t k, int64_t kvalid_b, float* d, int64_t ldd,
                      bi_stream_t stream);
 
-// bi_lmhead_grad_logits that also writes rows n_vocab_rows .. pad_rows - 1 of
-// the gradient as zeros (pad_rows within the last 256-row tile).
+// bi_lmhead_grad_logits that also writes rows n_vocab_rows .. pad_rows - 1
+// and columns n_tokens .. pad_cols - 1 of the gradient as zeros (pad_rows
+// within the last 256-row tile, pad_cols within the last 256-token tile).
 int lmhead_grad_logits_padded(const char* fn, const void* hidden, const void* weight,
                               int64_t n_tokens, int64_t n_vocab_rows, int64_t d,
                               int64_t hidden_stride, int64_t weight_stride, int64_t vocab_offset,
                               int64_t vocab, const int64_t* labels, int64_t ignore_index,
                               const float* lse, const float* token_weights, void* grad_logits,
-                              int64_t grad_stride, int64_t pad_rows, int32_t* status_flag,
-                              bi_stream_t stream);
+                              int64_t grad_stride, int64_t pad_rows, int64_t pad_cols,
+                              int32_t* status_flag, bi_stream_t stream);
 
 }  // namespace bi_internal
 

@@ -127,16 +127,23 @@ struct LmArgs {
   int64_t ldd;
   int dout_bf16;
   int64_t gpad;             // grad-logits kernel: rows n_voc .. gpad-1 of gout written as zeros
+  int64_t tpad;             //                     and columns n_tok .. tpad-1 of every row
   int64_t kvalid_h;         // transposed product: rows of the H-side operand that exist
 };
 
 // What a workgroup does with its fp32 tile of D = W . H^T:
 //   kModeStats     per-token statistics of each 256-row vocabulary tile;
 //   kModeGrad      the gradient of the logits, bf16, vocabulary-major;
-//   kModeProduct   D itself, fp32 or bf16, operands with K contiguous;
 //   kModeProductT  D added into an fp32 output, operands with M (N) contiguous:
-//                  "W" is stored [K][n_voc] and "H" [K][n_tok].
-enum { kModeStats = 0, kModeGrad = 1, kModeProduct = 2, kModeProductT = 3 };
+//                  "W" is stored [K][n_voc] and "H" [K][n_tok];
+//   kModeProductNT D itself, fp32 or bf16, "W" with K contiguous ([n_voc][K])
+//                  and "H" stored [K][n_tok].
+enum { kModeStats = 0, kModeGrad = 1, kModeProductT = 3, kModeProductNT = 4 };
+
+// Whether the "W" (A) and "H" (B) operands of a mode are stored [K][columns]
+// (read with transposing LDS reads) rather than with K contiguous.
+template <int MODE> constexpr bool kTransW = MODE == kModeProductT;
+template <int MODE> constexpr bool kTransH = MODE == kModeProductT || MODE == kModeProductNT;
 
 // Tile (tv, tn) of linear tile index t: groups of kGroup token tiles sweep
 // the vocabulary tiles together.
@@ -196,7 +203,8 @@ struct LmFill {
   const char* hbase;   // H row n0 (transposed: K-row 0, column n0)
   uint32_t ldw2, ldh2; // row pitches in bytes
   int wlast, hlast;    // last valid operand row within the tile
-  int row0;            // this lane's first row (transposed: its first K-row of a stage)
+  int row0;            // this lane's first row
+  int trow0;           // transposed side: this lane's first K-row of a stage
   uint32_t cbytes;     // byte offset of the chunk this lane's slot holds
   uint32_t lds0;       // this wave's first block: wave * 1 KB
   uint32_t wc, hc;     // transposed: the lane's chunk offset, clamped per side
@@ -216,7 +224,7 @@ __device__ inline const char* uniform_ptr(const char* q) {
 // the stage's 64 K-rows of the tile's 256 columns, 512 bytes each, and the
 // 16-byte chunk c of K-row k sits in chunk c ^ lm_swz_t(k).  A wave's request
 // covers two K-rows (1 KB); request i of a lane reads K-row
-// row0 + 2 kWaves i of the stage, clamped to the last K-row that exists, at
+// trow0 + 2 kWaves i of the stage, clamped to the last K-row that exists, at
 // the chunk its LDS position holds, clamped to the last chunk with columns in
 // the tile (so nothing is read past a row's end; the columns past the tile's
 // end are never stored).
@@ -227,31 +235,33 @@ __device__ inline int lm_swz_t(int k) { return 4 * (k & 3); }
 template <int MODE>
 __device__ inline LmFill lm_fill_setup(const LmArgs& p, int64_t v0, int64_t n0, int wave,
                                        int lane) {
-  LmFill f;
-  if constexpr (MODE == kModeProductT) {
-    f.row0 = 2 * wave + (lane >> 5);
-    const int lc = (lane & 31) ^ lm_swz_t(f.row0);   // lm_swz_t(row0 + 2 kWaves i) == lm_swz_t(row0)
-    f.wc = uint32_t(16 * min(lc, int((min(p.n_voc - v0, int64_t(kTV)) - 1) >> 3)));
-    f.hc = uint32_t(16 * min(lc, int((min(p.n_tok - n0, int64_t(kTN)) - 1) >> 3)));
-    f.wbase = uniform_ptr(reinterpret_cast<const char*>(p.weight + v0));
-    f.hbase = uniform_ptr(reinterpret_cast<const char*>(p.hidden + n0));
-    f.ldw2 = uint32_t(p.ldw * 2);
-    f.ldh2 = uint32_t(p.ldh * 2);
-    f.wklast = p.d - 1;
-    f.hklast = p.kvalid_h - 1;
-    f.lds0 = uint32_t(wave) * 1024u;
-    return f;
-  }
+  LmFill f{};
+  // K-contiguous side: 1 KB blocks of kBlockRows rows; transposed side: a
+  // wave's request covers two K-rows
   const int rb = lane / kChunks, slot = lane % kChunks;
   f.row0 = kBlockRows * wave + rb;
   f.cbytes = uint32_t(16 * (slot ^ lm_swz(f.row0)));   // lm_swz(row0 + 64 i) == lm_swz(row0)
-  f.wbase = uniform_ptr(reinterpret_cast<const char*>(p.weight + v0 * p.ldw));
-  f.hbase = uniform_ptr(reinterpret_cast<const char*>(p.hidden + n0 * p.ldh));
+  f.trow0 = 2 * wave + (lane >> 5);
+  const int lc = (lane & 31) ^ lm_swz_t(f.trow0);     // lm_swz_t(trow0 + 2 kWaves i) == lm_swz_t(trow0)
   f.ldw2 = uint32_t(p.ldw * 2);
   f.ldh2 = uint32_t(p.ldh * 2);
-  f.wlast = int(min(p.n_voc - v0, int64_t(kTV)) - 1);
-  f.hlast = int(min(p.n_tok - n0, int64_t(kTN)) - 1);
   f.lds0 = uint32_t(wave) * 1024u;
+  if constexpr (kTransW<MODE>) {
+    f.wc = uint32_t(16 * min(lc, int((min(p.n_voc - v0, int64_t(kTV)) - 1) >> 3)));
+    f.wbase = uniform_ptr(reinterpret_cast<const char*>(p.weight + v0));
+    f.wklast = p.d - 1;
+  } else {
+    f.wbase = uniform_ptr(reinterpret_cast<const char*>(p.weight + v0 * p.ldw));
+    f.wlast = int(min(p.n_voc - v0, int64_t(kTV)) - 1);
+  }
+  if constexpr (kTransH<MODE>) {
+    f.hc = uint32_t(16 * min(lc, int((min(p.n_tok - n0, int64_t(kTN)) - 1) >> 3)));
+    f.hbase = uniform_ptr(reinterpret_cast<const char*>(p.hidden + n0));
+    f.hklast = p.kvalid_h - 1;
+  } else {
+    f.hbase = uniform_ptr(reinterpret_cast<const char*>(p.hidden + n0 * p.ldh));
+    f.hlast = int(min(p.n_tok - n0, int64_t(kTN)) - 1);
+  }
   return f;
 }
 
@@ -279,11 +289,11 @@ template <int MODE>
 __device__ inline void lm_fill1(const LmFill& f, uint32_t slot, int stage, bool is_w, int i) {
   const char* base;
   uint32_t off;
-  if constexpr (MODE == kModeProductT) {
+  if (is_w ? kTransW<MODE> : kTransH<MODE>) {
     const int64_t k0 = int64_t(stage) * kBK;
     const uint32_t pitch = is_w ? f.ldw2 : f.ldh2;
     const int lim = int(min((is_w ? f.wklast : f.hklast) - k0, int64_t(kBK - 1)));
-    const int kr = min(f.row0 + 2 * kWaves * i, lim);
+    const int kr = min(f.trow0 + 2 * kWaves * i, lim);
     base = uniform_ptr((is_w ? f.wbase : f.hbase) + k0 * pitch);
     off = uint32_t(kr) * pitch + (is_w ? f.wc : f.hc);
   } else {
@@ -333,9 +343,9 @@ struct LmOffs {
 
 template <int MODE>
 __device__ inline LmOffs lm_offsets(int wv, int wt, int lane) {
-  LmOffs o;
+  LmOffs o{};
   const int lr = lane & 31, half = lane >> 5;
-  if constexpr (MODE == kModeProductT) {
+  if constexpr (kTransW<MODE> || kTransH<MODE>) {
     // ds_read_b64_tr_b16: within each 16-lane group, lane i receives the
     // 16-bit element i % 4 of the 8 bytes that lanes i / 4, 4 + i / 4,
     // 8 + i / 4 and 12 + i / 4 supply.  Lane 4e + q of group g supplies K-row
@@ -351,7 +361,8 @@ __device__ inline LmOffs lm_offsets(int wv, int wt, int lane) {
 #pragma unroll
     for (int y = 0; y < kYB; ++y)
       o.th[y] = lane_off + uint32_t(16 * ((((kWN * wt + 32 * y) >> 3) ^ lm_swz_t(e)) + cl));
-  } else {
+  }
+  if constexpr (!kTransW<MODE> || !kTransH<MODE>) {
 #pragma unroll
     for (int kk = 0; kk < kKS; ++kk) {
       const uint32_t in_row = uint32_t(lr * kRowBytes + 16 * ((2 * kk + half) ^ lm_swz(lr)));
@@ -379,19 +390,18 @@ __device__ inline bf16x8 lm_read_t(const char* p) {
 template <int MODE>
 __device__ inline void lm_read1(LmFrag& fr, const char* w, const char* h, const LmOffs& o,
                                 int kk, int j) {
-  if constexpr (MODE == kModeProductT) {
-    const int kbytes = 16 * kk * kTRowBytes;
-    if (j >= 1 && j <= kYB) {
+  const int kbytes = 16 * kk * kTRowBytes;
+  if (j >= 1 && j <= kYB) {
+    if constexpr (kTransH<MODE>)
       fr.b[j - 1] = lm_read_t(h + o.th[j - 1] + kbytes);
-    } else {
-      const int x = j == 0 ? 0 : j - kYB;
-      fr.a[x] = lm_read_t(w + o.tw[x] + kbytes);
-    }
-  } else if (j >= 1 && j <= kYB) {
-    fr.b[j - 1] = *reinterpret_cast<const bf16x8*>(h + o.h[kk] + (j - 1) * 32 * kRowBytes);
+    else
+      fr.b[j - 1] = *reinterpret_cast<const bf16x8*>(h + o.h[kk] + (j - 1) * 32 * kRowBytes);
   } else {
     const int x = j == 0 ? 0 : j - kYB;
-    fr.a[x] = *reinterpret_cast<const bf16x8*>(w + o.w[kk] + x * 32 * kRowBytes);
+    if constexpr (kTransW<MODE>)
+      fr.a[x] = lm_read_t(w + o.tw[x] + kbytes);
+    else
+      fr.a[x] = *reinterpret_cast<const bf16x8*>(w + o.w[kk] + x * 32 * kRowBytes);
   }
 }
 
@@ -714,7 +724,7 @@ void lmhead_kernel(LmArgs p) {
           if (i < p.n_voc) dout[i * p.ldd + j] += acc[x][y][r];
         }
       }
-  } else if constexpr (MODE == kModeProduct) {
+  } else if constexpr (MODE == kModeProductNT) {
     // D[i][j] for the rows and columns that exist; for a given accumulator
     // register the 64 lanes cover 32 consecutive columns of 2 rows
 #pragma unroll
@@ -805,23 +815,25 @@ void lmhead_kernel(LmArgs p) {
     wait_counts<63, 0>();
     lds_barrier();
     // rows v0 .. v0+255, 16-byte chunks of 8 tokens; 32 threads per row.
-    // Rows n_voc .. gpad-1 (the lm_head backward pads its chunk to whole K
-    // stages) are written as zeros.
+    // Rows n_voc .. gpad-1 and columns n_tok .. tpad-1 (the lm_head backward
+    // pads its chunk to whole K stages both ways) are written as zeros: the
+    // tile holds +0 for tokens past the end, which count as ignored, and
+    // tpad - 1 lies in the last token tile.
     const bool vec = (p.ldg % 8) == 0 && (reinterpret_cast<uintptr_t>(p.gout) % 16) == 0;
     constexpr int kChunksPerRow = kTN / 8;
 #pragma unroll 4
     for (int q = tid; q < kTV * kChunksPerRow; q += kThreads) {
       const int row = q / kChunksPerRow, c = q % kChunksPerRow;
       const int64_t i = v0 + row, j0 = n0 + 8 * c;
-      if (i >= p.gpad || j0 >= p.n_tok) continue;
+      if (i >= p.gpad || j0 >= p.tpad) continue;
       u32x4 v = *reinterpret_cast<const u32x4*>(ring + lm_grad_at(row, 8 * c));
       if (i >= p.n_voc) v = u32x4{0u, 0u, 0u, 0u};
       uint16_t* dst = p.gout + i * p.ldg + j0;
-      if (vec && j0 + 8 <= p.n_tok) {
+      if (vec && j0 + 8 <= p.tpad) {
         *reinterpret_cast<u32x4*>(dst) = v;
       } else {
         const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-        for (int e = 0; e < 8 && j0 + e < p.n_tok; ++e)
+        for (int e = 0; e < 8 && j0 + e < p.tpad; ++e)
           dst[e] = uint16_t(w4[e >> 1] >> (16 * (e & 1)));
       }
     }
@@ -884,36 +896,6 @@ int lm_launch(const char* fn, const LmArgs& a, bi_stream_t stream) {
 
 }  // namespace
 
-namespace bi_internal {
-
-// D[i][j] = sum_k A[i][k] B[j][k] on the lm_head kernel's pipeline (A in the
-// lm_head rows' place, B in the hidden states'); k a multiple of kBK.
-int lmhead_product(const char* fn, const void* a, int64_t a_rows, int64_t lda, const void* b,
-                   int64_t b_rows, int64_t ldb, int64_t k, void* d, int64_t ldd, bool d_bf16,
-                   bi_stream_t stream) {
-  if (k < kBK || k % kBK != 0 || k > (int64_t(1) << 22) || lda < k || ldb < k || lda % 8 ||
-      ldb % 8 || lda > (int64_t(1) << 22) || ldb > (int64_t(1) << 22) || ldd < b_rows)
-    return fail(BI_ERR_SHAPE, "%s: product shape outside the kernel's limits", fn);
-  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(d, d_bf16 ? 2 : 4))
-    return fail(BI_ERR_ALIGN, "%s: misaligned product operand", fn);
-  if (a_rows == 0 || b_rows == 0) return BI_OK;
-  LmArgs p{};
-  p.weight = static_cast<const uint16_t*>(a);
-  p.hidden = static_cast<const uint16_t*>(b);
-  p.n_voc = a_rows;
-  p.n_tok = b_rows;
-  p.d = k;
-  p.ldw = lda;
-  p.ldh = ldb;
-  p.dout = d;
-  p.ldd = ldd;
-  p.dout_bf16 = d_bf16 ? 1 : 0;
-  p.tiles_v = (a_rows + kTV - 1) / kTV;
-  p.tiles_n = (b_rows + kTN - 1) / kTN;
-  return lm_launch<kModeProduct>(fn, p, stream);
-}
-
-}  // namespace bi_internal
 
 extern "C" {
 
@@ -949,7 +931,7 @@ int bi_lmhead_grad_logits(const void* hidden, const void* weight, int64_t n_toke
   return lmhead_grad_logits_padded("bi_lmhead_grad_logits", hidden, weight, n_tokens,
                                    n_vocab_rows, d, hidden_stride, weight_stride, vocab_offset,
                                    vocab, labels, ignore_index, lse, token_weights, grad_logits,
-                                   grad_stride, n_vocab_rows, status_flag, stream);
+                                   grad_stride, n_vocab_rows, n_tokens, status_flag, stream);
 }
 
 }  // extern "C"
@@ -961,8 +943,8 @@ int lmhead_grad_logits_padded(const char* fn, const void* hidden, const void* we
                               int64_t hidden_stride, int64_t weight_stride, int64_t vocab_offset,
                               int64_t vocab, const int64_t* labels, int64_t ignore_index,
                               const float* lse, const float* token_weights, void* grad_logits,
-                              int64_t grad_stride, int64_t pad_rows, int32_t* status_flag,
-                              bi_stream_t stream) {
+                              int64_t grad_stride, int64_t pad_rows, int64_t pad_cols,
+                              int32_t* status_flag, bi_stream_t stream) {
   if (pad_rows < n_vocab_rows || pad_rows > (n_vocab_rows + kTV - 1) / kTV * kTV)
     return fail(BI_ERR_SHAPE, "%s: padded rows outside the last tile", fn);
   LmArgs a{};
@@ -972,6 +954,9 @@ int lmhead_grad_logits_padded(const char* fn, const void* hidden, const void* we
   if (grad_stride < n_tokens)
     return fail(BI_ERR_SHAPE, "%s: grad_stride %lld < n_tokens %lld", fn, (long long)grad_stride,
                 (long long)n_tokens);
+  if (pad_cols < n_tokens || pad_cols > (n_tokens + kTN - 1) / kTN * kTN ||
+      pad_cols > grad_stride)
+    return fail(BI_ERR_SHAPE, "%s: padded columns outside the last tile or the row", fn);
   if (n_tokens == 0 || n_vocab_rows == 0) return ok();
   if (!lse || !grad_logits) return fail(BI_ERR_NULL, "%s: lse and grad_logits are required", fn);
   if (!aligned(lse, 4) || !aligned(token_weights, 4) || !aligned(grad_logits, 2))
@@ -981,7 +966,40 @@ int lmhead_grad_logits_padded(const char* fn, const void* hidden, const void* we
   a.gout = static_cast<uint16_t*>(grad_logits);
   a.ldg = grad_stride;
   a.gpad = pad_rows;
+  a.tpad = pad_cols;
   return lm_launch<kModeGrad>(fn, a, stream);
+}
+
+// D[i][j] = sum_k A[i][k] B[k][j]: A [m][k] bf16 with rows of k contiguous
+// elements (its columns from kvalid_b on must be zero), B [k][n] bf16 with
+// rows of n contiguous elements of which only the first kvalid_b exist (the
+// rest read as row kvalid_b - 1); D fp32 or bf16 (RNE), overwritten.
+int lmhead_product_nt(const char* fn, const void* a, int64_t m, int64_t lda, const void* b,
+                      int64_t n, int64_t ldb, int64_t k, int64_t kvalid_b, void* d, int64_t ldd,
+                      bool d_bf16, bi_stream_t stream) {
+  if (k < kBK || k % kBK != 0 || k > (int64_t(1) << 22) || kvalid_b < 1 || kvalid_b > k ||
+      kvalid_b <= k - kBK || lda < k || ldb < n || lda % 8 || ldb % 8 ||
+      lda > (int64_t(1) << 22) || ldb > (int64_t(1) << 22) || ldd < n || m > 0x7fffffff ||
+      n > 0x7fffffff)
+    return fail(BI_ERR_SHAPE, "%s: product shape outside the kernel's limits", fn);
+  if (!aligned(a, 16) || !aligned(b, 16) || !aligned(d, d_bf16 ? 2 : 4))
+    return fail(BI_ERR_ALIGN, "%s: misaligned product operand", fn);
+  if (m == 0 || n == 0) return BI_OK;
+  LmArgs p{};
+  p.weight = static_cast<const uint16_t*>(a);
+  p.hidden = static_cast<const uint16_t*>(b);
+  p.n_voc = m;
+  p.n_tok = n;
+  p.d = k;
+  p.ldw = lda;
+  p.ldh = ldb;
+  p.kvalid_h = kvalid_b;
+  p.dout = d;
+  p.ldd = ldd;
+  p.dout_bf16 = d_bf16 ? 1 : 0;
+  p.tiles_v = (m + kTV - 1) / kTV;
+  p.tiles_n = (n + kTN - 1) / kTN;
+  return lm_launch<kModeProductNT>(fn, p, stream);
 }
 
 // D[i][j] += sum_k A[k][i] B[k][j]: A [k][m] and B [k][n] bf16 with rows of

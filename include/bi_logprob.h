@@ -305,29 +305,26 @@ BI_API int bi_lmhead_grad_logits(const void* hidden, const void* weight, int64_t
  * lm_head backward of "ZeroSyncGRPOTrainer - #6949": bf16 GEMMs with fp32
  * accumulation).  The vocabulary block is processed in chunks of as many
  * rows (a multiple of 256) as the workspace holds: per chunk the grad-logits
- * kernel, then G @ weight and G^T @ hidden, all on `stream`.  G @ weight
- * runs on the lm_head kernel's matrix-core pipeline, which reads G
- * (vocabulary-major) and the lm_head rows as they are stored through
- * transposing LDS reads, while n_tokens rounded up to 8 is at most 2^22;
- * otherwise on hipBLASLt.  When n_tokens is a multiple of 64 (at most 2^22)
- * and the workspace also holds the hidden states transposed
- * (bi_lmhead_backward_workspace counts them), G^T @ hidden runs on the same
- * pipeline from that copy, made once per call; otherwise on hipBLASLt.
- * Each hipBLASLt GEMM shape keeps the algorithm chosen on its first call.
+ * kernel writes G (bf16, vocabulary-major, padded with zeros to whole 64-deep
+ * K stages: rows to a multiple of 64, tokens to n_tokens rounded up to 64),
+ * then G @ weight and G^T @ hidden run on the lm_head kernel's matrix-core
+ * pipeline, reading G, the lm_head rows and the hidden states as they are
+ * stored (transposing LDS reads where an operand is stored [K][columns]), all
+ * on `stream`.  grad_weight rows are the same bits whatever the chunking;
+ * grad_hidden sums the chunks in order (same bits for the same workspace size
+ * on every run).
  *   grad_hidden    [n_tokens, grad_hidden_stride] fp32, ACCUMULATED (zero it
  *                  for a fresh gradient; vocabulary shards add their parts)
  *   grad_weight    [n_vocab_rows, grad_weight_stride] of grad_weight_dtype
  *                  (BI_F32 or BI_BF16), overwritten
  *   workspace      device memory, 256-byte aligned, of workspace_bytes >=
  *                  bi_lmhead_backward_workspace(n_tokens, d, chunk_rows) for
- *                  chunks of chunk_rows (at least 256 rows of G beside the
- *                  library's part; the transposed copy when it fits); it is
- *                  in use until the queued work ends
- * Sizes and strides must fit in 32 bits.  The first call on a device that
- * needs hipBLASLt creates the library's handle (which allocates); nothing
- * else allocates.  Calls that need hipBLASLt are serialized between host
- * threads; the others run concurrently (each with its own workspace).
- * n_tokens == 0 or n_vocab_rows == 0 writes nothing. */
+ *                  chunks of chunk_rows (at least one 256-row chunk of G); it
+ *                  is in use until the queued work ends
+ * n_tokens <= 2^22; other sizes and strides must fit in 32 bits, and d and
+ * the strides follow bi_lmhead_tile_stats.  Nothing is allocated and nothing
+ * synchronizes; calls on different streams with their own workspaces run
+ * concurrently.  n_tokens == 0 or n_vocab_rows == 0 writes nothing. */
 BI_API int bi_lmhead_backward(const void* hidden, const void* weight, int64_t n_tokens,
                               int64_t n_vocab_rows, int64_t d, int64_t hidden_stride,
                               int64_t weight_stride, int64_t vocab_offset, int64_t vocab,
@@ -339,10 +336,9 @@ BI_API int bi_lmhead_backward(const void* hidden, const void* weight, int64_t n_
                               bi_stream_t stream);
 
 /* Workspace bytes for bi_lmhead_backward with chunks of chunk_rows lm_head
- * rows (rounded up to a multiple of 256), hidden size d: 128 MiB for
- * hipBLASLt (reserved whether or not a call needs it), the transposed hidden
- * states when n_tokens is a multiple of 64, and the chunk of G; -1 for bad
- * arguments. */
+ * rows (rounded up to a multiple of 256): one chunk of G, its rows by
+ * n_tokens rounded up to 64, in bf16; -1 for bad arguments (negative sizes,
+ * chunk_rows < 1, n_tokens > 2^22).  d is validated only. */
 BI_API int64_t bi_lmhead_backward_workspace(int64_t n_tokens, int64_t d, int64_t chunk_rows);
 
 /* Human-readable name of a status code (static string). */

@@ -192,10 +192,12 @@ def test_lmhead_backward_argument_errors(L):
     f = L.bi_lmhead_backward
     ws = L.bi_lmhead_backward_workspace
     need = ws(8, 128, 256)
-    assert need == (128 << 20) + 256 * 8 * 2 and ws(9, 128, 1) == (128 << 20) + 256 * 16 * 2
-    # 64 tokens: room for the transposed hidden states too
-    assert ws(64, 128, 256) == (128 << 20) + 128 * 64 * 2 + 256 * 64 * 2
+    # one chunk of G: its rows (a multiple of 256) by the tokens padded to 64
+    assert need == 256 * 64 * 2 and ws(9, 128, 1) == 256 * 64 * 2
+    assert ws(64, 128, 257) == 512 * 64 * 2 and ws(65, 128, 256) == 256 * 128 * 2
+    assert ws(1 << 22, 128, 256) == 256 * (1 << 22) * 2
     assert ws(-1, 128, 256) == -1 and ws(8, 128, 0) == -1 and ws(8, -1, 256) == -1
+    assert ws((1 << 22) + 1, 128, 256) == -1
     args = dict(h=P, w=P, n=8, vc=300, d=128, ldh=128, ldw=128, off=0, v=300, lab=P, lse=P,
                 gh=P, ldgh=128, gw=P, gdt=bi.BI_BF16, ldgw=128, ws=ctypes.c_void_p(0x100000),
                 wsb=need)
@@ -208,7 +210,8 @@ def test_lmhead_backward_argument_errors(L):
 
     assert call(gdt=7) == bi.BI_ERR_DTYPE
     assert call(ldgh=100) == bi.BI_ERR_SHAPE       # gradient stride below d
-    assert call(n=1 << 31) == bi.BI_ERR_SHAPE      # beyond the library GEMM's 32-bit sizes
+    assert call(n=1 << 31) == bi.BI_ERR_SHAPE
+    assert call(n=(1 << 22) + 1) == bi.BI_ERR_SHAPE   # beyond the pipeline's 2^22-element rows
     assert call(ws=NUL) == bi.BI_ERR_NULL
     assert call(gh=NUL) == bi.BI_ERR_NULL
     assert call(ws=ctypes.c_void_p(0x100010)) == bi.BI_ERR_ALIGN

@@ -111,9 +111,9 @@ def test_lmhead_statistics_replay():
 
 
 def test_lmhead_backward_replays():
-    # grad-logits kernel plus two library GEMMs per vocabulary chunk; the
-    # workspace and the outputs are the caller's, so the graph owns nothing
-    n, vc, d, chunk = 320, 1000, 128, 256   # 320 tokens: the matrix-core G^T . hidden
+    # grad-logits kernel plus two matrix-core products per vocabulary chunk;
+    # the workspace and the outputs are the caller's, so the graph owns nothing
+    n, vc, d, chunk = 300, 1000, 128, 256   # 300 tokens: G padded to 320 columns
     b = wl.lmhead_batch(n, vc, d, seed=45, ignore_frac=0.05)
     to_bf16 = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda() \
         .view(torch.bfloat16)

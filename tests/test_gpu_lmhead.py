@@ -261,28 +261,38 @@ def test_backward_against_oracle(n, vc, d, chunk, gdt):
     _check_grads(host(gh), host(gw.float()), G, h, w, gdt == torch.bfloat16)
 
 
-@pytest.mark.parametrize("n,vc,d,chunk,pad", [(256, 1000, 128, 256, 0), (640, 1030, 192, 512, 0),
-                                              (256, 700, 128, 512, 64)])
+@pytest.mark.parametrize("n,vc,d,pad", [(256, 1000, 128, 0), (300, 1030, 192, 0),
+                                        (77, 700, 128, 64)])
 @pytest.mark.parametrize("gdt", [torch.float32, torch.bfloat16], ids=["gw_f32", "gw_bf16"])
-def test_backward_with_the_matrix_core_product(n, vc, d, chunk, pad, gdt):
-    # n_tokens a multiple of 64: G^T @ hidden runs on the lm_head kernel from
-    # the transposed hidden states; with a workspace one byte short of that
-    # copy plus one 256-row chunk the library takes it; both meet the bound
+def test_backward_workspace_sizes(n, vc, d, pad, gdt):
+    # every token count runs on the matrix-core pipeline: G is padded with zero
+    # columns to a whole 64-deep K stage (the workspace starts as NaN bytes, so
+    # a padding column left unwritten would show).  Workspaces of one 256-row
+    # chunk, of a chunk that does not divide the shard, one byte short of a
+    # chunk, and of the whole shard: grad_weight is the same bits for every
+    # chunking (each row is one product), grad_hidden (summed over chunks in
+    # their order) meets the bound each time
     b, H, W, labels, h, w, olse, tw = _setup(n, vc, d, seed=n + d + pad)
     if pad:
         H = _padded(H, pad)
     lse, lse_o = _saved_lse(olse)
     G = orc.lmhead_backward(h, w, b.labels, lse_o, tw)
-    need = int(bi.lib().bi_lmhead_backward_workspace(n, d, chunk))
-    copy = need - (128 << 20) - chunk * n * 2          # the transposed hidden states
-    assert copy >= n * d * 2
-    short = (128 << 20) + copy + 256 * n * 2 - 1
-    for wsb in (need, short):
-        ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    one = int(bi.lib().bi_lmhead_backward_workspace(n, d, 256))
+    assert one == 256 * (-(-n // 64) * 64) * 2
+    gws = []
+    for wsb in (one, 3 * one - 1, int(bi.lib().bi_lmhead_backward_workspace(n, d, vc))):
+        ws = torch.full((wsb,), 255, dtype=torch.uint8, device="cuda")
         gh, gw = bi.lmhead_backward(H, W, labels, lse, dev(tw), grad_weight_dtype=gdt,
-                                    chunk_rows=chunk, workspace=ws)
+                                    workspace=ws)
         torch.cuda.synchronize()
         _check_grads(host(gh), host(gw.float()), G, h, w, gdt == torch.bfloat16)
+        gws.append(gw)
+    for other in gws[1:]:
+        assert torch.equal(gws[0].view(torch.int16 if gdt == torch.bfloat16 else torch.int32),
+                           other.view(torch.int16 if gdt == torch.bfloat16 else torch.int32))
+    ws = torch.empty(one - 1, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError):
+        bi.lmhead_backward(H, W, labels, lse, dev(tw), workspace=ws)
 
 
 def _padded(t, extra):
@@ -314,7 +324,7 @@ def test_padded_row_strides_give_the_same_bits():
     assert torch.equal(st.view(torch.int32), stp.view(torch.int32))
     for other in (gp, g8, g3):
         assert torch.equal(g.contiguous().view(torch.int16), other.contiguous().view(torch.int16))
-    # the backward with padded operands: the library GEMMs take the strides
+    # the backward with padded operands
     gh, gw = bi.lmhead_backward(Hp, Wp, labels, lse, twd, chunk_rows=512)
     torch.cuda.synchronize()
     G = orc.lmhead_backward(h, w, b.labels, lse_o, tw)

@@ -1,6 +1,6 @@
 """Concurrent use: two host threads, each on its own stream, call the library
 at the same time (the row kernels, the lm_head statistics and the lm_head
-backward with its library GEMMs) on different inputs; every result must equal
+backward) on different inputs; every result must equal
 the one computed alone on the default stream, bit for bit."""
 import threading
 
