@@ -24,7 +24,8 @@ import torch  # first: the library then binds to the HIP runtime torch has loade
 __all__ = [
     "IGNORE_INDEX", "BiError", "fwd", "bwd", "fwd_bwd", "policy_loss_fwd_bwd", "vocab_chunk_stats", "stats_combine",
     "row_geometry", "fwd_multi", "diff_stats", "lmhead_tile_stats", "lmhead_logprob",
-    "lmhead_tile_rows", "lmhead_grad_logits", "lmhead_backward", "lmhead_logprob_entropy",
+    "lmhead_tile_rows", "lmhead_grad_logits", "lmhead_backward", "lmhead_backward_noalloc",
+    "lmhead_logprob_entropy",
     "LogprobEntropy", "logprob_entropy", "lib",
     "library_path",
 ]
@@ -103,6 +104,9 @@ def lib() -> ctypes.CDLL:
     L.bi_lmhead_backward.argtypes = [vp, vp, i64, i64, i64, i64, i64, i64, i64, vp, i64, vp, vp,
                                      vp, i64, vp, i32, i64, vp, i64, vp, vp]
     L.bi_lmhead_backward.restype = i32
+    L.bi_lmhead_backward_noalloc.argtypes = [vp, vp, i64, i64, i64, i64, i64, i64, i64, vp,
+                                             i64, vp, vp, vp, i64, vp, i32, i64, vp, vp]
+    L.bi_lmhead_backward_noalloc.restype = i32
     L.bi_lmhead_backward_workspace.argtypes = [i64, i64, i64]
     L.bi_lmhead_backward_workspace.restype = i64
     L.bi_stats_combine.argtypes = [vp, i64, i64, vp, i64, vp, vp, vp, vp]
@@ -486,6 +490,35 @@ def lmhead_backward(hidden: torch.Tensor, weight: torch.Tensor, labels: torch.Te
             ignore_index, _ptr(lse), _ptr(token_weights), _ptr(grad_hidden), ldgh,
             _ptr(grad_weight), _dtype_code(grad_weight.dtype), ldgw, _ptr(workspace),
             workspace.numel() * workspace.element_size(), _ptr(status), hs))
+    return grad_hidden, grad_weight
+
+
+def lmhead_backward_noalloc(hidden: torch.Tensor, weight: torch.Tensor, labels: torch.Tensor,
+                            lse: torch.Tensor, token_weights: Optional[torch.Tensor],
+                            grad_hidden: torch.Tensor, grad_weight: torch.Tensor,
+                            vocab_offset: int = 0, vocab: Optional[int] = None,
+                            ignore_index: int = IGNORE_INDEX, *,
+                            status: Optional[torch.Tensor] = None, stream=None):
+    """lmhead_backward into the caller's grad_hidden (accumulated) and grad_weight,
+    with no workspace: the library's static device scratch holds the logits
+    gradient (at most 131,072 tokens).  Nothing is allocated, here or in the
+    library; calls that may overlap on one GPU race on that scratch."""
+    n, d, ldh, vc, ldw = _lmhead_operands(hidden, weight, labels)
+    _vec(lse, n, torch.float32, "lse")
+    _vec(token_weights, n, torch.float32, "token_weights")
+    _vec(status, 1, torch.int32, "status")
+    vocab = vocab_offset + vc if vocab is None else vocab
+    _, dh, ldgh = _rows(grad_hidden, "grad_hidden")
+    if grad_hidden.dtype != torch.float32 or grad_hidden.shape[0] != n or dh != d:
+        raise ValueError(f"grad_hidden must be a float32 [{n}, {d}] tensor")
+    _, dgw, ldgw = _rows(grad_weight, "grad_weight")
+    if grad_weight.shape[0] != vc or dgw != d:
+        raise ValueError(f"grad_weight must be a [{vc}, {d}] tensor")
+    with _on_stream(stream) as hs:
+        _check("bi_lmhead_backward_noalloc", lib().bi_lmhead_backward_noalloc(
+            _ptr(hidden), _ptr(weight), n, vc, d, ldh, ldw, vocab_offset, vocab, _ptr(labels),
+            ignore_index, _ptr(lse), _ptr(token_weights), _ptr(grad_hidden), ldgh,
+            _ptr(grad_weight), _dtype_code(grad_weight.dtype), ldgw, _ptr(status), hs))
     return grad_hidden, grad_weight
 
 

@@ -335,6 +335,39 @@ BI_API int bi_lmhead_backward(const void* hidden, const void* weight, int64_t n_
                               void* workspace, int64_t workspace_bytes, int32_t* status_flag,
                               bi_stream_t stream);
 
+/* Size of the static device scratch of bi_lmhead_backward_noalloc (64 MiB on
+ * every GPU the library runs on, held until the process ends) and the most
+ * tokens it serves: one 256-row chunk of the logits gradient, bf16, with the
+ * tokens rounded up to 64. */
+#define BI_LMHEAD_NOALLOC_SCRATCH_BYTES (64 << 20)
+#define BI_LMHEAD_NOALLOC_MAX_TOKENS 131072
+
+/* bi_lmhead_backward without a workspace, for callers that cannot allocate
+ * or pass device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, outputs and arithmetic as
+ * bi_lmhead_backward, with G's chunks in a static device array of
+ * BI_LMHEAD_NOALLOC_SCRATCH_BYTES instead of the caller's workspace: the
+ * results are bit-identical to bi_lmhead_backward given a workspace of that
+ * many bytes.  The array's device address is looked up once per device, on
+ * the first call made with that device current.
+ *   n_tokens  at most BI_LMHEAD_NOALLOC_MAX_TOKENS (131,072); more returns
+ *             BI_ERR_SHAPE before anything is queued
+ * Nothing is allocated (no hipMalloc, no library allocation).  Every call on
+ * one GPU uses that GPU's one array: calls that may overlap on one GPU (on
+ * different streams, or from host threads whose calls are not ordered on one
+ * stream) race and give wrong results; calls queued on one stream are
+ * ordered and safe.  Nothing in the array needs to start at zero: each chunk
+ * writes every element of G that its products read. */
+BI_API int bi_lmhead_backward_noalloc(const void* hidden, const void* weight, int64_t n_tokens,
+                                      int64_t n_vocab_rows, int64_t d, int64_t hidden_stride,
+                                      int64_t weight_stride, int64_t vocab_offset,
+                                      int64_t vocab, const int64_t* labels,
+                                      int64_t ignore_index, const float* lse,
+                                      const float* token_weights, float* grad_hidden,
+                                      int64_t grad_hidden_stride, void* grad_weight,
+                                      int grad_weight_dtype, int64_t grad_weight_stride,
+                                      int32_t* status_flag, bi_stream_t stream);
+
 /* Workspace bytes for bi_lmhead_backward with chunks of chunk_rows lm_head
  * rows (rounded up to a multiple of 256): one chunk of G, its rows by
  * n_tokens rounded up to 64, in bf16; -1 for bad arguments (negative sizes,

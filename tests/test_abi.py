@@ -40,7 +40,7 @@ def test_header_declares_the_four_entry_points():
                "bi_logprob_fwd_bwd", "bi_policy_loss_fwd_bwd", "bi_logprob_fwd_multi",
                "bi_logprob_diff_stats", "bi_lmhead_tile_stats", "bi_lmhead_tiles",
                "bi_lmhead_tile_rows", "bi_lmhead_grad_logits", "bi_lmhead_backward",
-               "bi_lmhead_backward_workspace"):
+               "bi_lmhead_backward_workspace", "bi_lmhead_backward_noalloc"):
         assert fn in names
 
 
@@ -292,3 +292,23 @@ def test_a_c_program_links_and_calls_the_abi(tmp_path):
     r = subprocess.run([exe], capture_output=True, text=True, env=env, timeout=60)
     assert r.returncode == 0, (r.returncode, r.stdout, r.stderr)
     assert "1024 threads" in r.stdout and "bi_logprob_fwd(n_rows = -1)" in r.stdout
+
+
+def test_lmhead_backward_noalloc_argument_errors(L):
+    # host checks only: every error below returns before the device is touched
+    f = L.bi_lmhead_backward_noalloc
+    args = dict(n=8, vc=300, d=128, lse=P, gh=P, gw=P, gdt=bi.BI_BF16, ldgh=128)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(P, P, a["n"], a["vc"], a["d"], 128, 128, 0, a["vc"], P, -100, a["lse"], NUL,
+                 a["gh"], a["ldgh"], a["gw"], a["gdt"], 128, NUL, NUL)
+
+    assert call(n=131072 + 1) == bi.BI_ERR_SHAPE          # beyond the static scratch
+    assert b"static scratch" in L.bi_last_error()
+    assert call(gdt=5) == bi.BI_ERR_DTYPE
+    assert call(ldgh=64) == bi.BI_ERR_SHAPE
+    assert call(gh=NUL) == bi.BI_ERR_NULL
+    assert call(lse=NUL) == bi.BI_ERR_NULL
+    assert call(gh=ctypes.c_void_p(0x10002)) == bi.BI_ERR_ALIGN
+    assert call(n=0) == bi.BI_OK and call(vc=0) == bi.BI_OK
