@@ -140,28 +140,40 @@ __device__ inline float tree_sum(const float* e) {
   }
 }
 
-// Accumulate NV vectors (NV*VEC decoded values, in lane order) into `a`.
-template <int VEC, int NV>
-__device__ inline void accumulate(Acc& a, const float* z) {
-  const float mx = tree_max<NV * VEC>(z, a.m);
+// The two halves of accumulate.  First the group's max over its N values
+// moves `a` to the new reference, which is returned ...
+template <int N>
+__device__ inline float accumulate_rebase(Acc& a, const float* z) {
+  const float mx = tree_max<N>(z, a.m);
   const float c = ref_of(mx);
   rebase(a, c);
   a.m = mx;
+  return c;
+}
+
+// ... then each vector's VEC values add their terms about it.
+template <int VEC>
+__device__ inline void accumulate_terms(Acc& a, const float* z, float c) {
+  float e[VEC], tc[VEC];
 #pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    float e[VEC], tc[VEC];
-#pragma unroll
-    for (int k = 0; k < VEC; ++k) {
-      const float t = fmaf(z[j * VEC + k], kLog2e, c);
-      e[k] = exp2_hw(t);              // 0 for z = -inf; NaN for NaN z
-      tc[k] = fmaxf(t, kTFloor);      // finite, so 0 * tc == 0 for masked columns
-    }
-    float u = e[0] * tc[0];
-#pragma unroll
-    for (int k = 1; k < VEC; ++k) u = fmaf(e[k], tc[k], u);
-    a.S += tree_sum<VEC>(e);
-    a.U += u;
+  for (int k = 0; k < VEC; ++k) {
+    const float t = fmaf(z[k], kLog2e, c);
+    e[k] = exp2_hw(t);              // 0 for z = -inf; NaN for NaN z
+    tc[k] = fmaxf(t, kTFloor);      // finite, so 0 * tc == 0 for masked columns
   }
+  float u = e[0] * tc[0];
+#pragma unroll
+  for (int k = 1; k < VEC; ++k) u = fmaf(e[k], tc[k], u);
+  a.S += tree_sum<VEC>(e);
+  a.U += u;
+}
+
+// Accumulate NV vectors (NV*VEC decoded values, in lane order) into `a`.
+template <int VEC, int NV>
+__device__ inline void accumulate(Acc& a, const float* z) {
+  const float c = accumulate_rebase<NV * VEC>(a, z);
+#pragma unroll
+  for (int j = 0; j < NV; ++j) accumulate_terms<VEC>(a, z + j * VEC, c);
 }
 
 }  // namespace

@@ -34,6 +34,8 @@
 //    path with the same column map and arithmetic.
 
 
+#include <atomic>
+
 #include "bi_common.h"
 
 namespace {
@@ -704,11 +706,18 @@ struct FusedArgs {
 // r = exp(logprob - old), surrogate min(r A, clip(r, 1 - lo, 1 + hi) A), loss
 // = -c * surrogate, weight = -d loss / d logprob = c A r where the unclipped
 // term is the minimum (ties count as unclipped), else 0.
-__device__ inline float policy_weight(const FusedArgs& p, int64_t row, float logprob,
+// The inputs of a row that the forward's finish needs besides the logits:
+// its label logit and, for the policy loss, the behaviour logprob, the
+// advantage and the loss scale.
+struct RowScalars {
+  float zy, old_logprob, advantage, scale;
+};
+
+__device__ inline float policy_weight(const FusedArgs& p, const RowScalars& in, float logprob,
                                       float* loss) {
-  const float r = exp2_hw((logprob - p.old_logprob[row]) * kLog2e);
-  const float A = p.advantages[row];
-  const float c = p.loss_scale ? p.loss_scale[row] : 1.0f;
+  const float r = exp2_hw((logprob - in.old_logprob) * kLog2e);
+  const float A = in.advantage;
+  const float c = in.scale;
   const float rc = fminf(fmaxf(r, 1.0f - p.clip_low), 1.0f + p.clip_high);
   const bool unclipped = r * A <= rc * A;
   *loss = -c * (unclipped ? r * A : rc * A);
@@ -731,14 +740,16 @@ __device__ inline float policy_weight(const FusedArgs& p, int64_t row, float log
 
 // The forward half of a fused row.  Every lane gets the lse and the weight of
 // the gradient (the given one, or the policy-loss weight when POLICY).
-template <bool POLICY>
-__device__ inline void fused_finish_forward(const FusedArgs& p, int64_t row, const Acc& a,
-                                            float* lds, int T, int tid, float zy, bool ignored,
-                                            bool bad, float* lse_out, float* w_out) {
+// `scalars()` is called by thread 0 after the block reduction.
+template <bool POLICY, typename Scalars>
+__device__ inline void fused_finish(const FusedArgs& p, int64_t row, const Acc& a, float* lds,
+                                    int T, int tid, bool ignored, bool bad, Scalars&& scalars,
+                                    float* lse_out, float* w_out) {
   const Acc r = block_reduce(a, lds, T, tid);
   if (tid == 0) {
+    const RowScalars in = scalars();
     const float lse = lse_of(r);
-    const float lp = bad ? NAN : (ignored ? 0.0f : zy - lse);
+    const float lp = bad ? NAN : (ignored ? 0.0f : in.zy - lse);
     if (p.lse) p.lse[row] = lse;
     if (p.entropy) p.entropy[row] = entropy_of(r);
     if (p.logprob) p.logprob[row] = lp;
@@ -746,7 +757,7 @@ __device__ inline void fused_finish_forward(const FusedArgs& p, int64_t row, con
     lds[3 * kMaxWaves] = lse;
     if constexpr (POLICY) {
       float loss = bad ? NAN : 0.0f, w = bad ? NAN : 0.0f;
-      if (!ignored && !bad) w = policy_weight(p, row, lp, &loss);
+      if (!ignored && !bad) w = policy_weight(p, in, lp, &loss);
       if (p.loss) p.loss[row] = loss;
       if (p.weight_out) p.weight_out[row] = w;
       lds[3 * kMaxWaves + 1] = w;
@@ -755,6 +766,22 @@ __device__ inline void fused_finish_forward(const FusedArgs& p, int64_t row, con
   __syncthreads();
   *lse_out = lds[3 * kMaxWaves];
   if constexpr (POLICY) *w_out = lds[3 * kMaxWaves + 1];
+}
+
+// fused_finish with the row's inputs loaded by thread 0 when needed.
+template <bool POLICY>
+__device__ inline void fused_finish_forward(const FusedArgs& p, int64_t row, const Acc& a,
+                                            float* lds, int T, int tid, float zy, bool ignored,
+                                            bool bad, float* lse_out, float* w_out) {
+  fused_finish<POLICY>(p, row, a, lds, T, tid, ignored, bad, [&] {
+    RowScalars in{zy, 0.0f, 0.0f, 1.0f};
+    if (POLICY && !ignored && !bad) {
+      in.old_logprob = p.old_logprob[row];
+      in.advantage = p.advantages[row];
+      in.scale = p.loss_scale ? p.loss_scale[row] : 1.0f;
+    }
+    return in;
+  }, lse_out, w_out);
 }
 
 template <int DT, int GT, bool ALIGNED, bool POLICY>
@@ -797,6 +824,269 @@ void fused_reread_kernel(FusedArgs p) {
       bwd_row<DT, GT, false, false, P2, REV>(b, src, dst, y, kind, lse, w, T, tid);
     if (row + gridDim.x < p.n_rows) __syncthreads();
   }
+}
+
+// ------------------------------------- fused forward + backward, row on chip
+//
+// bf16 rows of 131,073 .. 155,648 columns (a multiple of 8; the Qwen3
+// vocabulary is one), 16-byte aligned: the geometry gives 1,024 lanes and
+// FS full steps plus RAG ragged one per lane, 17 to 19 vectors, which the
+// lane keeps in registers (4 VGPRs each).  One workgroup per compute unit
+// walks rows b, b + grid, ...:
+//  * pass 1 reduces the row from the registers in row_scan's exact order
+//    (groups of two steps, then a single step, then the ragged step), and
+//    block_reduce / lse / entropy are the row kernels' own, so every output
+//    is bit-identical to bi_logprob_fwd;
+//  * the row's first kPark vectors then move to LDS (each lane owns its slots
+//    k * 1,024 + lane, so no barrier guards them) and the freed registers
+//    take the next row's first kPark vectors, requested before the block
+//    reduction so that they land during it;
+//  * pass 2 writes the gradient (the first kPark vectors from LDS, the rest
+//    from registers) with bwd_vec's arithmetic, bit-identical to
+//    bi_logprob_bwd, and refills each register of steps kPark.. from the
+//    next row as soon as its gradient is computed.
+// So each element is read from HBM once and the gradient written once, with
+// the next row in flight while this one is reduced and written.  The kernel
+// holds no value in scratch memory (about 120 VGPRs of 128).
+//
+// Waiting.  Vector memory operations complete in order, and stores count
+// with loads, so a wait for one load also waits for everything issued before
+// it.  The kernel is laid out so that no wait is for more than it needs:
+// each refill load goes out before its vector's gradient store, the row's
+// label, weight, policy inputs and label logit come a row ahead through the
+// scalar data cache (counted by lgkmcnt instead), and the first row is
+// peeled off the loop so that the loop's head is reached with the same
+// operations in flight on both paths.
+
+constexpr int kOnchipThreads = 1024;
+constexpr int kPark = 9;   // vectors per lane parked in LDS: 9 x 16 KB per workgroup
+
+// A pointer that is the same in every lane, held in SGPRs.
+__device__ inline const char* sgpr_ptr(const char* q) {
+  const uint64_t v = reinterpret_cast<uint64_t>(q);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
+  return reinterpret_cast<const char*>((uint64_t(hi) << 32) | lo);
+}
+
+// Scalar loads (s_load, into SGPRs) of a row's inputs: the kernel never
+// writes them, and the scalar cache starts each dispatch invalidated.  The
+// loads are inline assembly, and the value passes through the wait (also
+// inline assembly), so no use can be scheduled before it.
+__device__ inline uint32_t sload32(const void* q) {
+  uint32_t v;
+  asm volatile("s_load_dword %0, %1, 0x0" : "=s"(v) : "s"(q) : "memory");
+  return v;
+}
+__device__ inline uint64_t sload64(const void* q) {
+  uint64_t v;
+  asm volatile("s_load_dwordx2 %0, %1, 0x0" : "=s"(v) : "s"(q) : "memory");
+  return v;
+}
+__device__ inline void swait(uint32_t& v) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+s"(v) : : "memory");
+}
+__device__ inline void swait(uint64_t& v) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+s"(v) : : "memory");
+}
+
+// A row's label (int64 bits), weight, behaviour logprob, advantage and loss
+// scale (fp32 bits).
+struct OnchipRowIn {
+  uint64_t y;
+  uint32_t w, old_lp, adv, scale;
+};
+
+template <bool POLICY>
+__device__ inline OnchipRowIn onchip_row_in(const FusedArgs& p, int64_t row) {
+  OnchipRowIn in;
+  in.y = sload64(p.labels + row);
+  in.w = (!POLICY && p.weights) ? sload32(p.weights + row) : 0x3f800000u;
+  in.old_lp = POLICY ? sload32(p.old_logprob + row) : 0u;
+  in.adv = POLICY ? sload32(p.advantages + row) : 0u;
+  in.scale = (POLICY && p.loss_scale) ? sload32(p.loss_scale + row) : 0x3f800000u;
+  return in;
+}
+
+template <bool POLICY>
+__device__ inline void onchip_row_wait(OnchipRowIn& in) {
+  swait(in.y);
+  swait(in.w);
+  if constexpr (POLICY) {
+    swait(in.old_lp);
+    swait(in.adv);
+    swait(in.scale);
+  }
+}
+
+// The dword holding the bf16 logit of column y of a row that starts on a
+// 4-byte boundary (its columns are y & ~1 and y | 1, both in the row when
+// the width is even), and the logit itself.
+__device__ inline uint32_t sload_label_logit(const char* row, int64_t y) {
+  return sload32(row + (y & ~int64_t(1)) * 2);
+}
+__device__ inline float label_logit_of(uint32_t dword, int64_t y) {
+  return __uint_as_float((y & 1) ? (dword & 0xffff0000u) : (dword << 16));
+}
+
+template <int GT, bool POLICY, int FS, bool RAG>
+__global__ __launch_bounds__(kOnchipThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
+void fused_onchip_kernel(FusedArgs p) {
+  constexpr int DT = BI_BF16, VEC = 8, T = kOnchipThreads;
+  constexpr int NS = FS + (RAG ? 1 : 0);      // vectors per lane
+  static_assert(NS > kPark && NS <= 19, "row held on chip");
+  __shared__ __attribute__((aligned(1024))) u32x4 park[kPark * T];
+  __shared__ float lds[3 * kMaxWaves + 2];
+  const int tid = threadIdx.x;
+  const int64_t width = p.vocab;
+  const uint32_t nfull = uint32_t(width / VEC);            // width % 8 == 0: all vectors full
+  const bool rag_lane = RAG && uint32_t(FS * T + tid) < nfull;   // holds a ragged-step vector
+  const int row_bytes = int(width * 2);
+
+  int64_t row = blockIdx.x;
+  if (row >= p.n_rows) return;   // the whole workgroup together
+  u32x4 r[NS];   // the row's vectors (steps 0 .. NS-1) in this lane
+
+  // prologue: the first row's inputs, label logit and vectors (the ragged
+  // step's vector is loaded by every lane: past the row's end the buffer
+  // descriptor's range check returns zeros)
+  OnchipRowIn in = onchip_row_in<POLICY>(p, row);
+  onchip_row_wait<POLICY>(in);
+  uint32_t zy_word = 0u;
+  if (int64_t(in.y) >= 0 && int64_t(in.y) < width) {
+    zy_word = sload_label_logit(p.logits + row * p.row_bytes, int64_t(in.y));
+    swait(zy_word);
+  }
+  {
+    RowSrc src = row_src(sgpr_ptr(p.logits + row * p.row_bytes), row_bytes, T, tid);
+    asm volatile("" : "+s"(src.step_bytes));
+#pragma unroll
+    for (int k = 0; k < NS; ++k) r[k] = fetch<true>(src, uint32_t(k));
+  }
+
+  // One row; false after the workgroup's last row.  The loop runs it once
+  // outside and then as its body, so that both ways into the loop's head
+  // leave the same memory operations in flight (the compiler's waits at the
+  // head are for the fewer of the two).
+  auto row_step = [&]() -> bool {
+    const int64_t next = row + gridDim.x;
+    const bool has_next = next < p.n_rows;
+    // this row's inputs are in scalar registers; the next row's are requested
+    OnchipRowIn in_next = in;
+    if (has_next) in_next = onchip_row_in<POLICY>(p, next);
+    const int64_t y = int64_t(in.y);
+    const bool ignored = y == p.ignore_index;
+    const bool bad = !ignored && (y < 0 || y >= width);
+    const int kind = ignored ? 1 : (bad ? 2 : 0);
+    const float zy = kind == 0 ? label_logit_of(zy_word, y) : 0.0f;
+
+    // pass 1: row_scan's order (groups of two steps, a single step, the
+    // ragged step), one group at a time: a group's vectors are copied out of
+    // their registers only after the previous group's terms are summed,
+    // through a zero computed from the running sums.  Without that the
+    // compiler decodes every group ahead and runs every group's max ahead of
+    // the sums, keeping all their values live.
+    Acc a = acc_empty();
+    auto vec_after = [&](int k, const Acc& acc) -> u32x4 {
+      uint32_t tok;
+      asm volatile("v_and_b32 %0, 0, %1\n\tv_and_b32 %0, %0, %2"
+                   : "=&v"(tok)
+                   : "v"(acc.S), "v"(acc.U));
+      u32x4 q = r[k];
+      asm volatile("v_or_b32 %0, %0, %1" : "+v"(q.x) : "v"(tok));
+      return q;
+    };
+#pragma unroll
+    for (int g = 0; g < FS / 2; ++g) {
+      float z[2 * VEC];
+      const u32x4 v0 = vec_after(2 * g, a), v1 = vec_after(2 * g + 1, a);
+      Elt<DT>::decode(v0, z);
+      Elt<DT>::decode(v1, z + VEC);
+      accumulate<VEC, 2>(a, z);
+    }
+    if constexpr (FS % 2 == 1) {
+      float z[VEC];
+      Elt<DT>::decode(vec_after(FS - 1, a), z);
+      accumulate<VEC, 1>(a, z);
+    }
+    if constexpr (RAG) {
+      // lanes past the row's end take -inf, which adds exactly nothing
+      float z[VEC];
+      Elt<DT>::decode(vec_after(FS, a), z);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) z[e] = rag_lane ? z[e] : -INFINITY;
+      accumulate<VEC, 1>(a, z);
+    }
+
+    // the row's first kPark vectors move to LDS (this lane's slots), and the
+    // registers they free take the next row's first kPark vectors, requested
+    // now, before the block reduction: they are the first the next row's
+    // pass 1 needs, and nothing issued later (this row's gradient stores)
+    // has to land before them
+    RowSrc nsrc = row_src(sgpr_ptr(p.logits + (has_next ? next : row) * p.row_bytes), row_bytes,
+                          T, tid);
+    asm volatile("" : "+s"(nsrc.step_bytes));
+#pragma unroll
+    for (int k = 0; k < kPark; ++k) park[k * T + tid] = r[k];
+    // (after the last row these reload it: no branch around the loads, so
+    // the compiler's count of what is in flight is the same on every path)
+#pragma unroll
+    for (int k = 0; k < kPark; ++k) r[k] = fetch<true>(nsrc, uint32_t(k));
+    if (has_next) {
+      // the next row's label has arrived: request its label logit
+      onchip_row_wait<POLICY>(in_next);
+      const int64_t yn = int64_t(in_next.y);
+      if (yn >= 0 && yn < width) zy_word = sload_label_logit(p.logits + next * p.row_bytes, yn);
+    }
+
+    float lse, w = (!POLICY && kind == 0) ? __uint_as_float(in.w) : 1.0f;
+    fused_finish<POLICY>(p, row, a, lds, T, tid, ignored, bad, [&] {
+      return RowScalars{zy, __uint_as_float(in.old_lp), __uint_as_float(in.adv),
+                        __uint_as_float(in.scale)};
+    }, &lse, &w);
+
+    // pass 2: the gradient of each vector (the first kPark from LDS); each
+    // register is refilled from the next row as soon as its gradient is
+    // computed, the load issued before the store.  Every element is written
+    // as w * p (bwd_vec's arithmetic); the label's element, w * (p - 1), is
+    // written over it afterwards by the lane that holds it (one lane's
+    // stores to one address land in program order), so the bits are
+    // bi_logprob_bwd's.  Ignored rows get +0.0 and bad labels NaN, whatever
+    // their logits.
+    const RowDst<GT, VEC> dst(p.grad + row * p.grad_row_bytes, T, tid);
+    const bool live = kind == 0;
+    const float fill = kind == 1 ? 0.0f : NAN;
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+      // decoded afresh (from a copy the compiler cannot see through), not
+      // kept from pass 1
+      u32x4 q = k < kPark ? park[k * T + tid] : r[k];
+      asm volatile("" : "+v"(q.x), "+v"(q.y), "+v"(q.z), "+v"(q.w));
+      float z[VEC], g[VEC];
+      Elt<DT>::decode(q, z);
+      grad_vec<VEC>(z, lse, w, g);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) g[e] = live ? g[e] : fill;
+      if (k >= kPark) {
+        r[k] = fetch<true>(nsrc, uint32_t(k));
+        __builtin_amdgcn_sched_barrier(0);   // the load goes out before the store
+      }
+      if (k < FS || rag_lane) dst.template store<true>(uint32_t(k), g);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (live && uint32_t(tid) == uint32_t(y / VEC) % uint32_t(T))
+      dst.store1(y, w * (prob(zy, lse) - 1.0f));
+
+    if (!has_next) return false;
+    swait(zy_word);
+    in = in_next;
+    row = next;
+    __syncthreads();   // lds (the reduction's) is reused by the next row
+    return true;
+  };
+  if (row_step())
+    while (row_step()) {
+    }
 }
 
 // ------------------------------------------------ several labels per row
@@ -1048,6 +1338,60 @@ void launch_bwd(const BwdArgs& a, int threads, hipStream_t s) {
     hipLaunchKernelGGL((bwd_kernel<DT, GT, false>), grid, block, 0, s, a);
 }
 
+#ifndef BI_FUSED_ONCHIP
+#define BI_FUSED_ONCHIP 1
+#endif
+
+// Compute units of the current device (cached per device).
+int compute_units() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+// The row-on-chip fused kernel for bf16 rows of 1,024-lane geometry whose
+// vectors fit the registers (17..19 per lane), every vector full, logits rows
+// 16-byte aligned and gradient rows 4-byte aligned; false: the re-read kernel.
+template <bool POLICY>
+bool launch_fused_onchip(const FusedArgs& a, int grad_dtype, hipStream_t s) {
+  if (!BI_FUSED_ONCHIP) return false;
+  const int64_t nvec = a.vocab / 8;
+  if (a.vocab % 8 != 0 || nvec <= int64_t(16) * kOnchipThreads ||
+      nvec > int64_t(19) * kOnchipThreads)
+    return false;
+  if (!aligned(a.logits, 16) || a.row_bytes % 16 != 0 ||
+      !rows_dword_aligned(a.grad, a.grad_row_bytes))
+    return false;
+  const int fs = int(nvec / kOnchipThreads);
+  const bool rag = nvec % kOnchipThreads != 0;
+  const int64_t cus = compute_units();
+  const dim3 grid(unsigned(a.n_rows < cus ? a.n_rows : cus)), block(kOnchipThreads);
+#define BI_ONCHIP(GT, FS, RAG) \
+  hipLaunchKernelGGL((fused_onchip_kernel<GT, POLICY, FS, RAG>), grid, block, 0, s, a)
+#define BI_ONCHIP_GT(FS, RAG)                                   \
+  do {                                                          \
+    if (grad_dtype == BI_BF16) BI_ONCHIP(BI_BF16, FS, RAG);     \
+    else BI_ONCHIP(BI_F32, FS, RAG);                            \
+  } while (0)
+  if (fs == 16 && rag) BI_ONCHIP_GT(16, true);
+  else if (fs == 17 && !rag) BI_ONCHIP_GT(17, false);
+  else if (fs == 17) BI_ONCHIP_GT(17, true);
+  else if (fs == 18 && !rag) BI_ONCHIP_GT(18, false);
+  else if (fs == 18) BI_ONCHIP_GT(18, true);
+  else BI_ONCHIP_GT(19, false);
+#undef BI_ONCHIP_GT
+#undef BI_ONCHIP
+  return true;
+}
+
 template <bool POLICY>
 int launch_fused(const char* fn, FusedArgs a, int dtype, int grad_dtype, int64_t row_stride,
                  int64_t grad_row_stride, bi_stream_t stream) {
@@ -1070,11 +1414,24 @@ int launch_fused(const char* fn, FusedArgs a, int dtype, int grad_dtype, int64_t
     return fail(BI_ERR_ALIGN, "%s: misaligned pointer", fn);
   a.row_bytes = row_stride * int64_t(elem_size(dtype));
   a.grad_row_bytes = grad_row_stride * int64_t(elem_size(grad_dtype));
+  {
+    // the gradient is written while other rows' logits are still to be read
+    const uintptr_t l0 = reinterpret_cast<uintptr_t>(a.logits), g0 = reinterpret_cast<uintptr_t>(a.grad);
+    const uintptr_t l1 = l0 + uintptr_t((a.n_rows - 1) * a.row_bytes + a.vocab * int64_t(elem_size(dtype)));
+    const uintptr_t g1 = g0 + uintptr_t((a.n_rows - 1) * a.grad_row_bytes +
+                                        a.vocab * int64_t(elem_size(grad_dtype)));
+    if (l0 < g1 && g0 < l1)
+      return fail(BI_ERR_SHAPE, "%s: grad overlaps the logits (their byte ranges must be disjoint)",
+                  fn);
+  }
   const Geometry g = row_geometry(dtype, a.vocab);
   const bool all_aligned = rows_dword_aligned(a.logits, a.row_bytes) &&
                            rows_dword_aligned(a.grad, a.grad_row_bytes);
   const dim3 grid(grid_for(a.n_rows, g.threads)), block(g.threads);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == BI_BF16 && g.threads == kOnchipThreads &&
+      launch_fused_onchip<POLICY>(a, grad_dtype, s))
+    return launched(fn);
 #define BI_FUSED_LAUNCH(DT, GT)                                                              \
   do {                                                                                       \
     if (all_aligned)                                                                         \

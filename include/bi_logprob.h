@@ -155,7 +155,10 @@ BI_API int bi_logprob_bwd(const void* logits, int dtype, int64_t n_rows, int64_t
  * Why; Correctness and compatibility for the weights).
  *   weights      [n_rows] fp32, NULL means 1 (as in bi_logprob_bwd)
  *   logprob, entropy, lse  [n_rows] fp32 each; each may be NULL
- *   grad         required; layout and dtype rules as in bi_logprob_bwd
+ *   grad         required; layout and dtype rules as in bi_logprob_bwd.  Its
+ *                byte range must not overlap the logits' (BI_ERR_SHAPE):
+ *                rows' gradients are written while other rows are still
+ *                to be read.
  */
 BI_API int bi_logprob_fwd_bwd(const void* logits, int dtype, int64_t n_rows, int64_t vocab,
                               int64_t row_stride, const int64_t* labels, int64_t ignore_index,
@@ -181,6 +184,7 @@ BI_API int bi_logprob_fwd_bwd(const void* logits, int dtype, int64_t n_rows, int
  *   loss_scale   [n_rows] fp32, NULL means 1 (e.g. 1 / number of tokens)
  *   clip_low     in [0, 1); clip_high >= 0
  *   loss, weight [n_rows] fp32 outputs, each may be NULL
+ *   grad         as in bi_logprob_fwd_bwd (not overlapping the logits)
  */
 BI_API int bi_policy_loss_fwd_bwd(const void* logits, int dtype, int64_t n_rows, int64_t vocab,
                                   int64_t row_stride, const int64_t* labels,

@@ -116,9 +116,19 @@ def test_fused_argument_errors(L):
     assert fused(L, n=0, logits=NUL, labels=NUL, grad=NUL) == bi.BI_OK
 
 
-def policy(L, old=P, adv=P, lo=0.2, hi=0.28, n=4, loss=NUL):
+def test_fused_gradient_must_not_overlap_the_logits(L):
+    # 4 rows of 100 bf16 logits at P (bytes [P, P + 800)): the same buffer,
+    # the last row's last element, a buffer ending in the first element
+    for g in (0x10000, 0x10000 + 3 * 200 + 198, 0x10000 - 3 * 200 - 198):
+        assert fused(L, grad=ctypes.c_void_p(g)) == bi.BI_ERR_SHAPE, hex(g)
+        assert b"overlaps" in L.bi_last_error()
+    assert policy(L, grad=P) == bi.BI_ERR_SHAPE
+    assert b"overlaps" in L.bi_last_error()
+
+
+def policy(L, old=P, adv=P, lo=0.2, hi=0.28, n=4, loss=NUL, grad=P):
     return L.bi_policy_loss_fwd_bwd(P, bi.BI_BF16, n, 100, 100, P, -100, old, adv, NUL, lo, hi,
-                                    NUL, NUL, NUL, loss, NUL, P, bi.BI_BF16, 100, NUL, NUL)
+                                    NUL, NUL, NUL, loss, NUL, grad, bi.BI_BF16, 100, NUL, NUL)
 
 
 def test_policy_argument_errors(L):

@@ -510,3 +510,41 @@ def test_ignore_index_that_is_a_column(dt):
     omlp, _, _ = orc.forward_multi(z, host(mlab), ignore_index=ii)
     assert_close(host(mlp), omlp, tl, "multi logprob")
     assert np.all(host(mlp)[:, 1] == 0) and not np.any(np.signbit(host(mlp)[:, 1]))
+
+
+# bf16 widths whose 1,024-lane rows fit the registers (17 to 19 vectors per
+# lane): every (full steps, ragged step) class the row-on-chip fused kernel
+# has, 300 rows so that each workgroup walks more than one row (the next row's
+# vectors requested during this one), ignored rows and a bad label
+ONCHIP_WIDTHS = [131_080, 139_264, 139_272, 147_456, 147_464, 151_936, 155_648]
+
+
+@pytest.mark.parametrize("V", ONCHIP_WIDTHS)
+@pytest.mark.parametrize("gdt", [torch.bfloat16, torch.float32], ids=["g_bf16", "g_f32"])
+def test_fused_row_on_chip_equals_two_calls(V, gdt):
+    n = 300
+    b = random_batch(n, V, "bf16", seed=V % 1000, ignore_frac=0.1, mask_frac=0.01)
+    labels = b.labels.copy()
+    labels[7] = V + 3                              # a bad label: NaN row, flag raised
+    logits, dlab, w = dev_logits(b.logits, "bf16"), dev(labels), dev(b.weights)
+    flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+    flp, fent, flse, fg = bi.fwd_bwd(logits, dlab, w, gdt, status=flag)
+    lp, ent, lse = bi.fwd(logits, dlab)
+    g = bi.bwd(logits, dlab, lse, w, gdt)
+    torch.cuda.synchronize()
+    assert int(flag.item()) == bi.BI_FLAG_BAD_LABEL
+    i32 = torch.int32
+    for a, c in ((flp, lp), (fent, ent), (flse, lse)):
+        assert torch.equal(a.view(i32), c.view(i32))
+    gv = torch.int16 if gdt == torch.bfloat16 else torch.int32
+    assert torch.equal(fg.view(gv), g.view(gv))
+    assert torch.isnan(fg[7].float()).all() and torch.isnan(flp[7])
+    rows = np.array([0, 1, 255, 256, 257, 299])    # rows of a second walk included
+    z = orc.decode(b.logits[rows], "bf16")
+    olp, oent, olse = orc.forward(z, labels[rows])
+    tl, te, tg = TOL["bf16"]
+    assert_close(host(flp)[rows], olp, tl, "logprob")
+    assert_close(host(fent)[rows], oent, te, "entropy")
+    if gdt == torch.float32:
+        og = orc.backward(z, labels[rows], olse, b.weights[rows])
+        assert_close(host(fg)[rows], og, tg, "grad")
