@@ -841,10 +841,10 @@ void fused_reread_kernel(FusedArgs p) {
 //    k * 1,024 + lane, so no barrier guards them) and the freed registers
 //    take the next row's first kPark vectors, requested before the block
 //    reduction so that they land during it;
-//  * pass 2 writes the gradient (the first kPark vectors from LDS, the rest
-//    from registers) with bwd_vec's arithmetic, bit-identical to
-//    bi_logprob_bwd, and refills each register of steps kPark.. from the
-//    next row as soon as its gradient is computed.
+//  * pass 2 writes the gradient (first the vectors in registers, then those
+//    in LDS) with bwd_vec's arithmetic, bit-identical to bi_logprob_bwd, and
+//    refills each register of steps kPark.. from the next row as soon as
+//    its vector has been read.
 // So each element is read from HBM once and the gradient written once, with
 // the next row in flight while this one is reduced and written.  The kernel
 // holds no value in scratch memory (about 120 VGPRs of 128).
@@ -1045,19 +1045,24 @@ void fused_onchip_kernel(FusedArgs p) {
                         __uint_as_float(in.scale)};
     }, &lse, &w);
 
-    // pass 2: the gradient of each vector (the first kPark from LDS); each
-    // register is refilled from the next row as soon as its gradient is
-    // computed, the load issued before the store.  Every element is written
-    // as w * p (bwd_vec's arithmetic); the label's element, w * (p - 1), is
-    // written over it afterwards by the lane that holds it (one lane's
-    // stores to one address land in program order), so the bits are
-    // bi_logprob_bwd's.  Ignored rows get +0.0 and bad labels NaN, whatever
-    // their logits.
+    // pass 2: the gradient of each vector: first those still in registers
+    // (steps kPark ..), each register refilled from the next row as soon as
+    // its vector is read, the load issued before the store; then those in
+    // LDS (steps 0 .. kPark-1).  Memory operations complete in order, so the
+    // next row's pass 1, waiting for a refill, also waits for the stores
+    // issued before it: this order puts at most NS - kPark - 1 of them
+    // there, and the LDS vectors' stores behind every load.
+    // Every element is written as w * p (bwd_vec's arithmetic); the label's
+    // element, w * (p - 1), is written over it afterwards by the lane that
+    // holds it (one lane's stores to one address land in program order), so
+    // the bits are bi_logprob_bwd's.  Ignored rows get +0.0 and bad labels
+    // NaN, whatever their logits.
     const RowDst<GT, VEC> dst(p.grad + row * p.grad_row_bytes, T, tid);
     const bool live = kind == 0;
     const float fill = kind == 1 ? 0.0f : NAN;
 #pragma unroll
-    for (int k = 0; k < NS; ++k) {
+    for (int j = 0; j < NS; ++j) {
+      const int k = j < NS - kPark ? kPark + j : j - (NS - kPark);
       // decoded afresh (from a copy the compiler cannot see through), not
       // kept from pass 1
       u32x4 q = k < kPark ? park[k * T + tid] : r[k];
