@@ -220,7 +220,8 @@ __device__ inline const char* uniform_ptr(const char* q) {
   return reinterpret_cast<const char*>((uint64_t(hi) << 32) | lo);
 }
 
-// Transposed operands (kModeProductT) are stored [K][columns]: a unit holds
+// Transposed operands (both of kModeProductT, the H side of kModeProductNT)
+// are stored [K][columns]: a unit holds
 // the stage's 64 K-rows of the tile's 256 columns, 512 bytes each, and the
 // 16-byte chunk c of K-row k sits in chunk c ^ lm_swz_t(k).  A wave's request
 // covers two K-rows (1 KB); request i of a lane reads K-row
@@ -559,14 +560,15 @@ __device__ inline uint32_t pack_bf16(float lo, float hi) {
 // kModeGrad:    the gradient of the logits, w * (softmax - onehot) from the
 //               saved lse, written as bf16 (the cross-entropy backward of PR
 //               #4685 Summary, on the lm_head logits).
-// kModeProduct: the product itself, fp32 or bf16 (RNE), for the lm_head
-//               backward's G^T . hidden with the operands' roles taken by G
-//               and the transposed hidden states.
 // kModeProductT: the product of two operands stored [K][columns], added into
 //               an fp32 output: the lm_head backward's grad_hidden += G . W_c
 //               with G vocabulary-major and the lm_head rows as they are.
-// Same main loop, same product bits, in the first three modes; the fourth
-// reads its fragments with transposing LDS reads.
+// kModeProductNT: the product of one operand with K-contiguous rows and one
+//               stored [K][columns], written fp32 or bf16 (RNE): the lm_head
+//               backward's grad_W_c = G_c^T . hidden with G's rows (tokens
+//               contiguous) and the hidden states as they are.
+// Same main loop in every mode; the operands stored [K][columns] are read
+// with transposing LDS reads.
 template <int MODE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWavesPerEU, kWavesPerEU)))
 void lmhead_kernel(LmArgs p) {
