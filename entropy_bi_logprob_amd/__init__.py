@@ -484,6 +484,9 @@ def lmhead_backward(hidden: torch.Tensor, weight: torch.Tensor, labels: torch.Te
             raise ValueError(f"grad_weight must be a [{vc}, {d}] tensor")
         if workspace is None:
             nbytes = int(L.bi_lmhead_backward_workspace(n, d, min(chunk_rows, max(vc, 1))))
+            if nbytes < 0:
+                raise ValueError(f"no workspace size for {n} tokens, d {d}, "
+                                 f"chunk_rows {chunk_rows} (at most 2^22 tokens)")
             workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
         _check("bi_lmhead_backward", L.bi_lmhead_backward(
             _ptr(hidden), _ptr(weight), n, vc, d, ldh, ldw, vocab_offset, vocab, _ptr(labels),
