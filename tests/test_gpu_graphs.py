@@ -64,6 +64,36 @@ def test_fused_fwd_bwd_replays():
     replay_and_check(g, (lp, ent, lse, grad), ref, lambda r: bi.fwd(oz, oy))
 
 
+def test_fused_row_on_chip_and_policy_replay():
+    # the Qwen3 width in bf16: the kernel that keeps each row on chip, plain
+    # and with the clipped-ratio weights derived in it; 300 rows, so some
+    # workgroups walk a second row
+    n, v = 300, 151_936
+    b = wl.random_batch(n, v, "bf16", seed=45, ignore_frac=0.05, mask_frac=0.01)
+    z, y, w = dev_logits(b.logits, "bf16"), dev(b.labels), dev(b.weights)
+    gen = np.random.default_rng(46)
+    old = dev(gen.normal(-12.0, 1.0, n).astype(np.float32))
+    adv = dev(gen.standard_normal(n).astype(np.float32))
+    lp, ent, lse = (torch.empty(n, device="cuda") for _ in range(3))
+    grad = torch.empty_like(z)
+    plp, pent, plse, ploss, pw = (torch.empty(n, device="cuda") for _ in range(5))
+    pgrad = torch.empty((n, v), dtype=torch.float32, device="cuda")
+
+    def step():
+        bi.fwd_bwd(z, y, w, out=(lp, ent, lse), grad=grad)
+        bi.policy_loss_fwd_bwd(z, y, old, adv, 0.2, 0.28, grad=pgrad)
+
+    ref_fused = [t.clone() for t in bi.fwd_bwd(z, y, w)]
+    ref_policy = [t.clone() for t in bi.policy_loss_fwd_bwd(z, y, old, adv, 0.2, 0.28,
+                                                             grad_dtype=torch.float32)]
+    torch.cuda.synchronize()
+    g = capture(step)
+    o = wl.random_batch(64, v, "bf16", seed=47)
+    oz, oy = dev_logits(o.logits, "bf16"), dev(o.labels)
+    replay_and_check(g, (lp, ent, lse, grad, pgrad), ref_fused + [ref_policy[5]],
+                     lambda r: bi.fwd_bwd(oz, oy))
+
+
 def test_two_calls_and_chunked_path_replay():
     n, v = 513, 40_001
     b = wl.random_batch(n, v, "f32", seed=43, ignore_frac=0.05, mask_frac=0.05)
