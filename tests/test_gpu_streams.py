@@ -1,7 +1,8 @@
 """Concurrent use: two host threads, each on its own stream, call the library
-at the same time (the row kernels, the lm_head statistics and the lm_head
-backward) on different inputs; every result must equal
-the one computed alone on the default stream, bit for bit."""
+at the same time (the row kernels, among them the fused kernel that keeps each
+row on chip, the lm_head statistics and the lm_head backward) on different
+inputs; every result must equal the one computed alone on the default stream,
+bit for bit."""
 import threading
 
 import numpy as np
@@ -23,7 +24,9 @@ def to_bf16(bits):
 def make_case(seed):
     b = wl.random_batch(400, 30_000, "bf16", seed=seed, ignore_frac=0.05)
     h = wl.lmhead_batch(300, 1500, 128, seed=seed + 1, ignore_frac=0.05)
+    q = wl.random_batch(300, 151_936, "bf16", seed=seed + 2, ignore_frac=0.05)   # rows on chip
     return {"z": dev_logits(b.logits, "bf16"), "y": dev(b.labels), "w": dev(b.weights),
+            "zq": dev_logits(q.logits, "bf16"), "yq": dev(q.labels), "wq": dev(q.weights),
             "H": to_bf16(h.hidden), "W": to_bf16(h.weight), "hy": dev(h.labels),
             "tw": torch.linspace(-1.0, 1.0, 300, device="cuda")}
 
@@ -32,7 +35,8 @@ def run(case):
     lp, ent, lse, grad = bi.fwd_bwd(case["z"], case["y"], case["w"])
     hlp, hent, hlse = bi.lmhead_logprob(case["H"], case["W"], case["hy"])
     gh, gw = bi.lmhead_backward(case["H"], case["W"], case["hy"], hlse, case["tw"], chunk_rows=512)
-    return [lp, ent, lse, grad, hlp, hent, hlse, gh, gw]
+    qlp, qent, qlse, qgrad = bi.fwd_bwd(case["zq"], case["yq"], case["wq"])
+    return [lp, ent, lse, grad, hlp, hent, hlse, gh, gw, qlp, qent, qlse, qgrad]
 
 
 def same(a, b):
@@ -86,9 +90,10 @@ def test_explicit_side_stream(handle):
     hlp, hent, hlse = bi.lmhead_logprob(case["H"], case["W"], case["hy"], stream=arg)
     gh, gw = bi.lmhead_backward(case["H"], case["W"], case["hy"], hlse, case["tw"],
                                 chunk_rows=512, stream=arg)
+    qlp, qent, qlse, qgrad = bi.fwd_bwd(case["zq"], case["yq"], case["wq"], stream=arg)
     junk = [torch.full((1 << 22,), float(i), device="cuda") for i in range(16)]
     del junk
     s.synchronize()
-    outs = [lp, ent, lse, grad, hlp, hent, hlse, gh, gw]
+    outs = [lp, ent, lse, grad, hlp, hent, hlse, gh, gw, qlp, qent, qlse, qgrad]
     for k, (o, r) in enumerate(zip(outs, ref)):
         assert same(o, r), f"output {k} differs on a side stream"
