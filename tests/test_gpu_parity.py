@@ -562,9 +562,9 @@ def _padded(rows, stride, dtype):
 @pytest.mark.parametrize("n", [1, 257, 600])                  # one row; a second walk for a few
 def test_fused_row_on_chip_strided_rows_and_step_seams(V, n):   # workgroups; three walks
     # padded logits and gradient pitches, labels on the first and last column
-    # and on each side of every step seam (a step is 1,024 vectors of 8), the
-    # policy kernel with its in-kernel weights: each against the two calls on
-    # contiguous rows, bit for bit
+    # and on each side of every step seam (a step is 1,024 vectors of 8), a
+    # bad label, the policy kernel with its in-kernel weights: each against
+    # the two calls on contiguous rows, bit for bit
     b = random_batch(n, V, "bf16", seed=n + V % 977, ignore_frac=0.1, mask_frac=0.01)
     labels = b.labels.copy()
     seams = [0, V - 1] + [s * 8192 + d for s in range(1, V // 8192 + 1) for d in (-1, 0)
@@ -572,16 +572,20 @@ def test_fused_row_on_chip_strided_rows_and_step_seams(V, n):   # workgroups; th
     for i in range(n):
         if labels[i] != -100:
             labels[i] = seams[i % len(seams)]
+    if n > 1:
+        labels[1] = V + 5                                     # a bad label: NaN row, flag raised
     dense = dev_logits(b.logits, "bf16")
     logits = _padded(dense, V + 24, torch.bfloat16)          # 48 more bytes per row
     dlab, w = dev(labels), dev(b.weights)
     i32 = torch.int32
     for gdt, gpad in ((torch.bfloat16, 6), (torch.float32, 3)):
         grad = _padded(torch.full((n, V), float("nan"), dtype=gdt, device="cuda"), V + gpad, gdt)
-        flp, fent, flse, _ = bi.fwd_bwd(logits, dlab, w, grad=grad)
+        flag = torch.zeros(1, dtype=torch.int32, device="cuda")
+        flp, fent, flse, _ = bi.fwd_bwd(logits, dlab, w, grad=grad, status=flag)
         lp, ent, lse = bi.fwd(dense, dlab)
         g = bi.bwd(dense, dlab, lse, w, gdt)
         torch.cuda.synchronize()
+        assert int(flag.item()) == (bi.BI_FLAG_BAD_LABEL if n > 1 else 0)
         for a, c in ((flp, lp), (fent, ent), (flse, lse)):
             assert torch.equal(a.view(i32), c.view(i32))
         gv = torch.int16 if gdt == torch.bfloat16 else torch.int32
@@ -592,11 +596,16 @@ def test_fused_row_on_chip_strided_rows_and_step_seams(V, n):   # workgroups; th
     gen = np.random.default_rng([V, n])
     old = (olp - gen.uniform(-0.5, 0.5, n)).astype(np.float32)
     adv = gen.standard_normal(n).astype(np.float32)
+    pflag = torch.zeros(1, dtype=torch.int32, device="cuda")
     plp, pent, plse, loss, pw, pg = bi.policy_loss_fwd_bwd(
-        logits, dlab, dev(old), dev(adv), 0.2, 0.28, None, torch.bfloat16)
+        logits, dlab, dev(old), dev(adv), 0.2, 0.28, None, torch.bfloat16, status=pflag)
     lp, ent, lse = bi.fwd(dense, dlab)
     g = bi.bwd(dense, dlab, lse, pw, torch.bfloat16)
     torch.cuda.synchronize()
+    assert int(pflag.item()) == (bi.BI_FLAG_BAD_LABEL if n > 1 else 0)
+    if n > 1:
+        assert torch.isnan(plp[1]) and torch.isnan(pw[1]) and torch.isnan(loss[1])
+        assert torch.isnan(pg[1].float()).all()
     for a, c in ((plp, lp), (pent, ent), (plse, lse)):
         assert torch.equal(a.view(i32), c.view(i32))
     assert torch.equal(pg.view(torch.int16), g.view(torch.int16))
