@@ -516,7 +516,12 @@ def test_ignore_index_that_is_a_column(dt):
 # lane): every (full steps, ragged step) class the row-on-chip fused kernel
 # has, 300 rows so that each workgroup walks more than one row (the next row's
 # vectors requested during this one), ignored rows and a bad label
-ONCHIP_WIDTHS = [131_080, 139_264, 139_272, 147_456, 147_464, 151_936, 155_648]
+# every on-chip shape (17..19 vectors per lane, with and without a ragged
+# step), and just outside the band, where the re-reading kernel takes over:
+# 131,072 (512-lane geometry), 155,650 (not a multiple of 8), 155,656 (20
+# vectors per lane)
+ONCHIP_WIDTHS = [131_080, 139_264, 139_272, 147_456, 147_464, 151_936, 155_648,
+                 131_072, 155_650, 155_656]
 
 
 @pytest.mark.parametrize("V", ONCHIP_WIDTHS)
