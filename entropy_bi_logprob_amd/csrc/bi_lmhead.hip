@@ -832,7 +832,9 @@ void lmhead_kernel(LmArgs p) {
       if (i >= p.n_voc) v = u32x4{0u, 0u, 0u, 0u};
       uint16_t* dst = p.gout + i * p.ldg + j0;
       if (vec && j0 + 8 <= p.tpad) {
-        *reinterpret_cast<u32x4*>(dst) = v;
+        // non-temporal: G is read back only by the next kernels, long after
+        // this tile's operand lines have left L2
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
       } else {
         const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
         for (int e = 0; e < 8 && j0 + e < p.tpad; ++e)
