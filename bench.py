@@ -217,6 +217,21 @@ def lmhead_leg(bi, torch, np, wl, N, V, seed, steps, warm, stream, with_cpu=True
             "cpu_baseline": cpu}
 
 
+def blas_threads():
+    """Threads numpy's BLAS runs its matrix products on (threadpoolctl, else
+    OMP_NUM_THREADS), or None if neither says."""
+    try:
+        import numpy  # noqa: F401  (loads its BLAS, so that threadpoolctl finds it)
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads") for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n and all(isinstance(k, int) for k in n):
+            return max(n)
+    except Exception:
+        pass
+    v = os.environ.get("OMP_NUM_THREADS", "")
+    return int(v) if v.isdigit() else None
+
+
 def lmhead_cpu_baseline(b, np, wl, sample=2048):
     """The fp64 oracle on the first `sample` tokens of the lm_head workload: forward
     (logits, logprob, entropy) and backward (the gradient of the logits, grad_hidden
@@ -232,10 +247,9 @@ def lmhead_cpu_baseline(b, np, wl, sample=2048):
     orc.lmhead_backward(h, w, labels, lse, np.full(sample, -1.0 / sample))
     t2 = time.perf_counter()
     cores, _ = host_cpu()
-    blas = os.environ.get("OMP_NUM_THREADS", "unset")
     return {"fwd_tokens_per_s": sample / (t1 - t0), "fwd_bwd_tokens_per_s": sample / (t2 - t0),
-            "unit": "tokens/s", "cores": cores, "threads": f"BLAS threads (OMP_NUM_THREADS={blas})",
-            "kind": "oracle",
+            "unit": "tokens/s", "cores": cores, "threads": blas_threads(),
+            "threads_what": "BLAS threads of numpy's matrix products", "kind": "oracle",
             "sample": f"{sample} tokens x 151936 lm_head rows x d 2560, fp64 numpy "
                       f"(BLAS threads as configured), {t2 - t0:.1f} s wall"}
 

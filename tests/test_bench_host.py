@@ -93,3 +93,8 @@ def test_ceilings_library_exports_and_validates():
     assert L.bi_ceiling_copy(P, None, 160, None) == -1
     assert L.bi_ceiling_copy(P, P, -16, None) == -1
     assert L.bi_ceiling_read(P, 0, P, None) == 0             # nothing to do
+
+
+def test_blas_threads_is_a_count():
+    n = bench.blas_threads()
+    assert n is None or (isinstance(n, int) and n >= 1)
